@@ -1,0 +1,168 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) DeepSeek-V3.2-Exp MoE layer forward.
+ *
+ * The layer maps x [tokens, d_model] (bf16) to its MoE update of the same
+ * shape ("DeepSeek-V3.2-Exp · MoE update": output expression and shape;
+ * "DeepSeek-V3.2-Exp · Add shared output": formula).  The steps are exposed
+ * one by one (gate, permute, grouped FFN, combine) and fused (moe_forward);
+ * a fused residual-add RMSNorm ("MoE update", rmsnorm excerpt) precedes the
+ * layer when blocks are stacked.
+ *
+ * Conventions shared by every entry point:
+ *  - All array arguments are DEVICE pointers (HIP device memory) unless the
+ *    comment says "host".  Structs passed by pointer are host memory, read
+ *    during the call only.
+ *  - The caller owns every buffer.  The library allocates nothing, keeps no
+ *    state between calls and never synchronises the host: work is enqueued
+ *    on `stream` (a hipStream_t; NULL = the default stream) and a return of
+ *    MOE_OK means "enqueued".  Calls on different streams are independent as
+ *    long as their buffers (workspace included) do not overlap.
+ *  - bf16 tensors are passed as uint16_t (the bit pattern).  FP8 tensors are
+ *    OCP e4m3fn codes (uint8_t), with one float32 scale per 128x128 block.
+ *  - Row-major layouts throughout.  d_model and inter must be multiples of
+ *    128; n_experts <= 256; experts per group >= 2; topk <= 32.
+ *  - Errors: arguments are checked on the host before anything is enqueued;
+ *    a negative moe_status is returned and nothing runs.  A failed launch
+ *    returns MOE_ERR_HIP.  tokens == 0 is a valid no-op.
+ *  - Routing indices must lie in [0, n_experts) and be distinct within a
+ *    token.  Out-of-range indices are clamped into range and duplicates give
+ *    unspecified (but finite-memory, non-faulting) results.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, negative size, inconsistent dims */
+  MOE_ERR_UNSUPPORTED = -2, /* dims outside what the kernels implement */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than moe_workspace_size() */
+  MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as documented */
+  MOE_ERR_HIP = -5          /* a HIP launch failed */
+} moe_status;
+
+/* Layer shape (host struct).  DeepSeek-V3.2-Exp: {7168, 256, 8, 4, 8, 2048, 2.5}. */
+typedef struct {
+  int32_t d_model;     /* hidden size d ("MoE update": shape [B, T, 7168]) */
+  int32_t n_experts;   /* routed experts E ("Gate projection" breadcrumb: 256 routed experts) */
+  int32_t n_groups;    /* expert groups G; group g holds experts [g*E/G, (g+1)*E/G) */
+  int32_t topk_groups; /* groups kept per token */
+  int32_t topk;        /* experts selected per token K */
+  int32_t inter;       /* expert hidden size ("Gate projection": 2048 expert d_ff) */
+  float route_scale;   /* factor applied to the normalised router weights */
+} moe_dims;
+
+/* n SwiGLU experts with FP8 Linear layers ("Gate projection", expert and Linear
+ * excerpts): w1, w3 map d -> inter, w2 maps inter -> d; weights are [out, in]. */
+typedef struct {
+  const uint8_t* w1; /* e4m3fn [n][inter][d]    (16-byte aligned) */
+  const uint8_t* w3; /* e4m3fn [n][inter][d]    (16-byte aligned) */
+  const uint8_t* w2; /* e4m3fn [n][d][inter]    (16-byte aligned) */
+  const float* s1;   /* fp32  [n][inter/128][d/128] */
+  const float* s3;   /* fp32  [n][inter/128][d/128] */
+  const float* s2;   /* fp32  [n][d/128][inter/128] */
+} moe_experts;
+
+/* All parameters of one MoE layer.  The 256x7168 router weight plus a
+ * 256-element router bias are what the pages' count of 11,320,164,608 MoE
+ * parameters leaves after 257 experts ("MoE transformer block", parameter
+ * accounting table). */
+typedef struct {
+  const float* gate_w; /* fp32 [E][d] router weight */
+  const float* gate_b; /* fp32 [E]    router bias, added to the scores for selection only */
+  moe_experts routed;  /* n = E */
+  moe_experts shared;  /* n = 1, applied to every token ("Add shared output") */
+} moe_weights;
+
+/* Workspace bytes that any single entry point below (including moe_forward)
+ * needs for `tokens` tokens.  Returns 0 for invalid dims. */
+size_t moe_workspace_size(const moe_dims* dims, int64_t tokens);
+
+/* Router: ``weights, indices = self.gate(x)`` ("MoE update", moe-forward excerpt).
+ *   x       bf16 [T][d]   (16-byte aligned)
+ *   gate_w  fp32 [E][d]   (16-byte aligned), gate_b fp32 [E]
+ *   idx     int32 [T][K]  out: selected experts, descending biased score
+ *   w       fp32  [T][K]  out: sigmoid scores of idx normalised to sum 1, times route_scale
+ * Scores s = sigmoid(x . gate_w^T) are computed with fp32 accumulation; the
+ * selection uses b = s + gate_b: groups ranked by the sum of their two
+ * largest b, the top topk_groups groups kept, then the top K of b among the
+ * kept experts.  Ties go to the lower index.  Needs the workspace. */
+int moe_gate(const moe_dims* dims, int64_t tokens, const uint16_t* x, const float* gate_w,
+             const float* gate_b, int32_t* idx, float* w, void* workspace, size_t workspace_bytes,
+             void* stream);
+
+/* Token counting and expert-contiguous order (``bincount`` and
+ * ``torch.where(indices == i)``, "MoE update", moe-forward excerpt), plus the
+ * FP8 activation quantisation the expert Linear layers consume.
+ *   idx        int32 [T][K]      routing from moe_gate
+ *   x          bf16  [T][d]      (16-byte aligned)
+ *   counts     int32 [E]         out: rows per expert
+ *   offsets    int32 [E+1]       out: exclusive prefix sum of counts
+ *   row_token  int32 [T*K + T]   out: token of each permuted row; rows of expert e
+ *                                are [offsets[e], offsets[e+1]) in ascending token
+ *                                order; rows [T*K, T*K+T) are the shared expert's
+ *                                and hold 0..T-1
+ *   pair_row   int32 [T][K]      out: row of (token t, choice k)
+ *   xq         e4m3  [T][d]      out: per-128-block quantised x (16-byte aligned)
+ *   xs         fp32  [T][d/128]  out: block scales, amax/448 (1 for an all-zero block)
+ * Needs the workspace. */
+int moe_permute(const moe_dims* dims, int64_t tokens, const int32_t* idx, const uint16_t* x,
+                int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* pair_row,
+                uint8_t* xq, float* xs, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Grouped expert FFN over the permuted rows ("Gate projection": expert
+ * excerpt ``w2((silu(w1(x).float()) * w3(x).float()).type_as(x))``):
+ * for every row r of expert e (and every shared-expert row),
+ *   g = bf16(Q(x) . W1_e^T), u = bf16(Q(x) . W3_e^T), h = bf16(silu(g) * u),
+ *   out[r] = bf16(Q(h) . W2_e^T)
+ * with Q the per-128-block e4m3 activation quantiser and W the block-scaled
+ * FP8 weights.
+ *   routed, shared  expert weights (shared may be NULL: shared rows are then skipped)
+ *   offsets, row_token, xq, xs   from moe_permute
+ *   out             bf16 [T*K + T][d] out: one row per permuted row (16-byte aligned)
+ * Needs the workspace. */
+int moe_grouped_ffn(const moe_dims* dims, int64_t tokens, const moe_experts* routed,
+                    const moe_experts* shared, const int32_t* offsets, const int32_t* row_token,
+                    const uint8_t* xq, const float* xs, uint16_t* out, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Router-weighted combine plus shared output ("MoE update": ``y[idx] +=
+ * expert(x[idx]) * weights[idx, top]`` in ascending expert order, then
+ * ``y += shared_experts(x)``, then ``y.type_as(x)``):
+ *   delta[t] = bf16( sum over k in ascending idx[t][k] of w[t][k] * rows[pair_row[t][k]]
+ *                    + rows[T*K + t] )     accumulated in fp32.
+ *   rows    bf16 [T*K + T][d] from moe_grouped_ffn (16-byte aligned)
+ *   delta   bf16 [T][d] out (16-byte aligned)
+ * Pass has_shared = 0 to leave the shared rows out. */
+int moe_combine(const moe_dims* dims, int64_t tokens, const int32_t* idx, const float* w,
+                const int32_t* pair_row, const uint16_t* rows, int32_t has_shared,
+                uint16_t* delta, void* stream);
+
+/* The whole layer: gate -> permute -> grouped FFN -> combine, with no host
+ * synchronisation.  x bf16 [T][d] -> delta bf16 [T][d].  idx_out / w_out
+ * (int32 / fp32 [T][K]) receive the routing when non-NULL. */
+int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens,
+                const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/* Fused residual add + RMSNorm ("MoE update", rmsnorm excerpt, residual branch):
+ *   r = float(x) + float(residual);  residual <- bf16(r);
+ *   out = bf16(gain * r * rsqrt(mean(r^2) + eps))   (fp32 arithmetic)
+ *   x, residual, out  bf16 [T][d] (16-byte aligned; out may alias x); gain fp32 [d].
+ * d must be a multiple of 128 and at most 16384.  No workspace. */
+int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* residual,
+                    const float* gain, float eps, uint16_t* out, void* stream);
+
+/* Static description of a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,11 @@
+"""DeepSeek-V3.2-Exp MoE layer forward for one AMD MI355X (gfx950).
+
+The layer runs in hand-written HIP kernels behind the C ABI of include/moe.h
+(libmoe.so, built by ``python -m mixture_experts_ffn_bias_amd.build``); this
+package is its Python binding.
+"""
+from ._binding import (  # noqa: F401
+    LIB_PATH, SYMBOLS, MoeError, MoELayer, experts_struct, lib, make_dims, moe_add_rmsnorm, moe_combine,
+    moe_dims, moe_experts, moe_forward, moe_gate, moe_grouped_ffn, moe_permute, moe_weights, moe_workspace_size,
+    status_string, workspace,
+)

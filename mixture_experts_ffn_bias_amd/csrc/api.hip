@@ -1,0 +1,246 @@
+// C ABI of the MoE layer (declared in include/moe.h): argument checks on the
+// host, workspace carving, and the launches of the gfx950 kernels.  Nothing
+// here allocates device memory or synchronises the host.
+#include <math.h>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t WS_ALIGN = 256;
+
+struct Layout {
+  size_t zpart, idx, w, chunk_cnt, chunk_off, counts, offsets, row_token, pair_row, tiles, n_tiles, xq, xs, hq,
+      hs, rows, total;
+};
+
+size_t align_up(size_t v) { return (v + WS_ALIGN - 1) & ~(WS_ALIGN - 1); }
+
+Layout layout(const moe_dims& dm, int64_t T) {
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t E = dm.n_experts, K = dm.topk, d = dm.d_model, I = dm.inter, t = (size_t)T;
+  const size_t rows = t * K + t;
+  const size_t nchunks = (t + PERM_CHUNK - 1) / PERM_CHUNK;
+  const int NT = ffn_tile_rows(T);
+  L.zpart = take((size_t)gate_ksplit(T, dm.d_model, dm.n_experts) * t * E * 4);
+  L.idx = take(t * K * 4);
+  L.w = take(t * K * 4);
+  L.chunk_cnt = take(nchunks * E * 4);
+  L.chunk_off = take(nchunks * E * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.row_token = take(rows * 4);
+  L.pair_row = take(t * K * 4);
+  L.tiles = take((size_t)ffn_max_tiles(T, dm.topk, dm.n_experts, NT) * sizeof(int4));
+  L.n_tiles = take(4);
+  L.xq = take(t * d);
+  L.xs = take(t * (d / BLK) * 4);
+  L.hq = take(rows * I);
+  L.hs = take(rows * (I / BLK) * 4);
+  L.rows = take(rows * d * 2);
+  L.total = off;
+  return L;
+}
+
+int check_dims(const moe_dims* p) {
+  if (!p) return MOE_ERR_INVALID_ARG;
+  const moe_dims& d = *p;
+  if (d.d_model <= 0 || d.inter <= 0 || d.n_experts <= 0 || d.n_groups <= 0 || d.topk_groups <= 0 || d.topk <= 0)
+    return MOE_ERR_INVALID_ARG;
+  if (d.n_experts % d.n_groups != 0 || d.topk_groups > d.n_groups) return MOE_ERR_INVALID_ARG;
+  if (d.topk > d.topk_groups * (d.n_experts / d.n_groups)) return MOE_ERR_INVALID_ARG;
+  if (!isfinite(d.route_scale)) return MOE_ERR_INVALID_ARG;
+  if (d.d_model % BLK != 0 || d.inter % BLK != 0) return MOE_ERR_UNSUPPORTED;
+  if (d.d_model > 65536 || d.inter > 65536) return MOE_ERR_UNSUPPORTED;
+  if (d.n_experts > 256 || d.n_experts % 16 != 0) return MOE_ERR_UNSUPPORTED;
+  if (d.n_groups > 64 || d.n_experts / d.n_groups < 2) return MOE_ERR_UNSUPPORTED;
+  if (d.topk > 32) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int check_tokens(const moe_dims& d, int64_t T) {
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  // permuted rows (T*K routed + T shared) are indexed with int32
+  if (T > (int64_t)(0x7fffffff / (d.topk + 1))) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+int check_experts(const moe_experts* x) {
+  if (!x || !x->w1 || !x->w3 || !x->w2 || !x->s1 || !x->s3 || !x->s2) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x->w1, 16) || !aligned(x->w3, 16) || !aligned(x->w2, 16)) return MOE_ERR_ALIGN;
+  if (!aligned(x->s1, 4) || !aligned(x->s3, 4) || !aligned(x->s2, 4)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+ExpertPtrs ptrs(const moe_experts& x) { return ExpertPtrs{x.w1, x.w3, x.w2, x.s1, x.s3, x.s2}; }
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)            \
+  do {                           \
+    const int st_ = (expr);      \
+    if (st_ != MOE_OK) return st_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_workspace_size(const moe_dims* dims, int64_t tokens) {
+  if (check_dims(dims) != MOE_OK || check_tokens(*dims, tokens) != MOE_OK) return 0;
+  return layout(*dims, tokens).total;
+}
+
+int moe_gate(const moe_dims* dims, int64_t tokens, const uint16_t* x, const float* gate_w, const float* gate_b,
+             int32_t* idx, float* w, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  if (!x || !gate_w || !gate_b || !idx || !w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(gate_w, 16) || !aligned(gate_b, 4) || !aligned(idx, 4) || !aligned(w, 4))
+    return MOE_ERR_ALIGN;
+  const Layout L = layout(*dims, tokens);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
+  const moe_dims& d = *dims;
+  return hip_status(launch_gate(x, gate_w, gate_b, (int)tokens, d.d_model, d.n_experts, d.n_groups, d.topk_groups,
+                                d.topk, d.route_scale, at<float>(workspace, L.zpart),
+                                gate_ksplit(tokens, d.d_model, d.n_experts), idx, w, (hipStream_t)stream));
+}
+
+int moe_permute(const moe_dims* dims, int64_t tokens, const int32_t* idx, const uint16_t* x, int32_t* counts,
+                int32_t* offsets, int32_t* row_token, int32_t* pair_row, uint8_t* xq, float* xs, void* workspace,
+                size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  if (!idx || !x || !counts || !offsets || !row_token || !pair_row || !xq || !xs) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(idx, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
+      !aligned(row_token, 4) || !aligned(pair_row, 4) || !aligned(xs, 4))
+    return MOE_ERR_ALIGN;
+  const Layout L = layout(*dims, tokens);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
+  const moe_dims& d = *dims;
+  return hip_status(launch_permute(idx, x, (int)tokens, d.d_model, d.n_experts, d.topk,
+                                   at<int32_t>(workspace, L.chunk_cnt), at<int32_t>(workspace, L.chunk_off), counts,
+                                   offsets, row_token, pair_row, xq, xs, (hipStream_t)stream));
+}
+
+int moe_grouped_ffn(const moe_dims* dims, int64_t tokens, const moe_experts* routed, const moe_experts* shared,
+                    const int32_t* offsets, const int32_t* row_token, const uint8_t* xq, const float* xs,
+                    uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  MOE_TRY(check_experts(routed));
+  if (shared) MOE_TRY(check_experts(shared));
+  if (!offsets || !row_token || !xq || !xs || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(xq, 16) || !aligned(out, 16) || !aligned(offsets, 4) || !aligned(row_token, 4) || !aligned(xs, 4))
+    return MOE_ERR_ALIGN;
+  const Layout L = layout(*dims, tokens);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
+  const moe_dims& d = *dims;
+  const ExpertPtrs rp = ptrs(*routed);
+  ExpertPtrs sp;
+  if (shared) sp = ptrs(*shared);
+  return hip_status(launch_ffn(rp, shared ? &sp : nullptr, (int)tokens, d.d_model, d.inter, d.n_experts, d.topk,
+                               offsets, row_token, xq, xs, at<int4>(workspace, L.tiles),
+                               at<int32_t>(workspace, L.n_tiles), at<uint8_t>(workspace, L.hq),
+                               at<float>(workspace, L.hs), out, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_dims* dims, int64_t tokens, const int32_t* idx, const float* w, const int32_t* pair_row,
+                const uint16_t* rows, int32_t has_shared, uint16_t* delta, void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  if (!idx || !w || !pair_row || !rows || !delta) return MOE_ERR_INVALID_ARG;
+  if (!aligned(rows, 16) || !aligned(delta, 16) || !aligned(idx, 4) || !aligned(w, 4) || !aligned(pair_row, 4))
+    return MOE_ERR_ALIGN;
+  const moe_dims& d = *dims;
+  return hip_status(launch_combine(idx, w, pair_row, rows, has_shared ? 1 : 0, (int)tokens, d.topk, d.n_experts,
+                                   d.d_model, delta, (hipStream_t)stream));
+}
+
+int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
+                uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  if (!weights || !weights->gate_w || !weights->gate_b || !x || !delta) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_experts(&weights->routed));
+  MOE_TRY(check_experts(&weights->shared));
+  if (!aligned(x, 16) || !aligned(delta, 16) || !aligned(weights->gate_w, 16) || !aligned(weights->gate_b, 4) ||
+      (idx_out && !aligned(idx_out, 4)) || (w_out && !aligned(w_out, 4)))
+    return MOE_ERR_ALIGN;
+  const Layout L = layout(*dims, tokens);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
+  const moe_dims& d = *dims;
+  const hipStream_t s = (hipStream_t)stream;
+  const int T = (int)tokens;
+  int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
+  float* w = w_out ? w_out : at<float>(workspace, L.w);
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* row_token = at<int32_t>(workspace, L.row_token);
+  int32_t* pair_row = at<int32_t>(workspace, L.pair_row);
+  uint8_t* xq = at<uint8_t>(workspace, L.xq);
+  float* xs = at<float>(workspace, L.xs);
+  uint16_t* rows = at<uint16_t>(workspace, L.rows);
+  MOE_TRY(hip_status(launch_gate(x, weights->gate_w, weights->gate_b, T, d.d_model, d.n_experts, d.n_groups,
+                                 d.topk_groups, d.topk, d.route_scale, at<float>(workspace, L.zpart),
+                                 gate_ksplit(tokens, d.d_model, d.n_experts), idx, w, s)));
+  MOE_TRY(hip_status(launch_permute(idx, x, T, d.d_model, d.n_experts, d.topk, at<int32_t>(workspace, L.chunk_cnt),
+                                    at<int32_t>(workspace, L.chunk_off), at<int32_t>(workspace, L.counts), offsets,
+                                    row_token, pair_row, xq, xs, s)));
+  const ExpertPtrs rp = ptrs(weights->routed), sp = ptrs(weights->shared);
+  MOE_TRY(hip_status(launch_ffn(rp, &sp, T, d.d_model, d.inter, d.n_experts, d.topk, offsets, row_token, xq, xs,
+                                at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
+                                at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), rows, s)));
+  return hip_status(launch_combine(idx, w, pair_row, rows, 1, T, d.topk, d.n_experts, d.d_model, delta, s));
+}
+
+int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* residual, const float* gain, float eps,
+                    uint16_t* out, void* stream) {
+  if (d <= 0 || tokens < 0 || !(eps >= 0.f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
+  if (d % BLK != 0 || d > 16384) return MOE_ERR_UNSUPPORTED;
+  if (tokens > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  if (tokens == 0) return MOE_OK;
+  if (!x || !residual || !gain || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(gain, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+  return hip_status(launch_add_rmsnorm(x, residual, gain, eps, d, tokens, out, (hipStream_t)stream));
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported dimensions";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_ALIGN: return "misaligned pointer";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// Device helpers shared by the gfx950 kernels of the MoE layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr int BLK = 128;          // FP8 block size of weights and activations
+constexpr float E4M3_MAX = 448.f;  // largest finite e4m3fn value
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Round to nearest even bfloat16 (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+__device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
+
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// A 128-deep e4m3 block operand, decoded to bfloat16 (exact: every e4m3 value
+// is a bf16 value) as four 8-element MFMA operands.
+struct Frag {
+  v8bf k[4];
+};
+
+// 32 e4m3 bytes (the lane's share of one 128-deep block) -> Frag.
+__device__ __forceinline__ Frag decode_e4m3(v8i q) {
+  Frag f;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const v2bf a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[2 * s], 1.0f, false);
+    const v2bf b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[2 * s], 1.0f, true);
+    const v2bf c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[2 * s + 1], 1.0f, false);
+    const v2bf d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((unsigned)q[2 * s + 1], 1.0f, true);
+    f.k[s] = v8bf{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  }
+  return f;
+}
+
+// D(16x16) = A(16x128) . B(16x128)^T for one e4m3 block, as four chained
+// bf16 MFMAs (products exact, fp32 accumulation).  Lane l ends with
+// D[4*(l/16)+j][l%16], j = 0..3.  A and B use the same lane->k mapping.
+//
+// (The fp8 MFMA forms sum a block with roughly 16 significant bits; the bf16
+// path on decoded operands is exact to fp32 rounding, which the layer's
+// rounding points -- bf16 g, u, h and an e4m3 re-quantisation of h -- need.)
+__device__ __forceinline__ v4f block_dot(const Frag& a, const Frag& b) {
+  v4f p = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < 4; ++s) p = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.k[s], b.k[s], p, 0, 0, 0);
+  return p;
+}
+
+// D += A(16x32 bf16) . B(16x32 bf16)^T
+__device__ __forceinline__ v4f mfma_bf16(v8bf a, v8bf b, v4f c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Four floats -> four e4m3fn bytes, round to nearest even.  |v| must not
+// exceed 464 (the hardware conversion gives NaN above that).
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+  int v = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  v = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, v, true);
+  return (uint32_t)v;
+}
+
+// The 32 bytes one lane contributes to an e4m3 MFMA operand for K block
+// `p` (128 bytes): chunks [16g, 16g+16) and [64+16g, 64+16g+16), g = lane/16.
+// Each load instruction of a wave then covers 64 contiguous bytes per row.
+__device__ __forceinline__ v8i load_frag_e4m3(const uint8_t* row_k, int g) {
+  v4i lo = *(const v4i*)(row_k + 16 * g);
+  v4i hi = *(const v4i*)(row_k + 64 + 16 * g);
+  v8i r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+}  // namespace moe

@@ -1,0 +1,49 @@
+// Host-side launchers of the gfx950 kernels (one per kernel file).  Each
+// returns the hipError_t of its launch(es).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct ExpertPtrs {
+  const uint8_t* w1;
+  const uint8_t* w3;
+  const uint8_t* w2;
+  const float* s1;
+  const float* s3;
+  const float* s2;
+};
+
+// tokens per permutation chunk (one workgroup of the count / scatter kernels)
+constexpr int PERM_CHUNK = 256;
+
+// gate.hip
+int gate_ksplit(int64_t T, int d, int E);
+hipError_t launch_gate(const uint16_t* x, const float* gate_w, const float* gate_b, int T, int d, int E,
+                       int G, int TG, int K, float route_scale, float* zpart, int ksplit, int32_t* idx,
+                       float* w, hipStream_t s);
+
+// permute.hip
+hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, int E, int K,
+                          int32_t* chunk_cnt, int32_t* chunk_off, int32_t* counts, int32_t* offsets,
+                          int32_t* row_token, int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s);
+
+// ffn.hip
+int ffn_tile_rows(int64_t T);                       // rows per FFN tile for this token count
+int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
+hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E,
+                      int K, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
+                      const float* xs, int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs,
+                      uint16_t* out, hipStream_t s);
+
+// combine.hip
+hipError_t launch_combine(const int32_t* idx, const float* w, const int32_t* pair_row, const uint16_t* rows,
+                          int has_shared, int T, int K, int E, int d, uint16_t* delta, hipStream_t s);
+
+// norm.hip
+hipError_t launch_add_rmsnorm(const uint16_t* x, uint16_t* residual, const float* gain, float eps, int d,
+                              int64_t T, uint16_t* out, hipStream_t s);
+
+}  // namespace moe

@@ -52,6 +52,7 @@ import math
 from typing import Dict, Optional, Sequence
 
 import numpy as np
+import torch
 
 BLOCK = 128          # "Gate projection", Linear excerpt: block_size = 128
 E4M3_MAX = 448.0     # largest finite e4m3fn value (OCP 8-bit floating point, E4M3)
@@ -85,6 +86,7 @@ def e4m3_table() -> np.ndarray:
 
 _E4M3 = e4m3_table()
 _E4M3_POS = _E4M3[:127]  # codes 0x00..0x7E: 0 .. 448, strictly increasing
+_E4M3_T = torch.from_numpy(_E4M3)
 
 
 def e4m3_decode(codes) -> np.ndarray:
@@ -139,14 +141,18 @@ def f64_to_bf16_bits(v) -> np.ndarray:
 # --------------------------------------------------------------------------
 
 def dequant_weight(codes, scale) -> np.ndarray:
-    """W[o, i] = e4m3(codes[o, i]) * scale[o // 128, i // 128], float64 [out, in]."""
-    codes = np.asarray(codes, dtype=np.uint8)
+    """W[o, i] = e4m3(codes[o, i]) * scale[o // 128, i // 128], float64 [out, in].
+
+    (The table lookup and the scaling run as multi-threaded torch CPU ops;
+    both are exact in float64.)
+    """
+    codes = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
     scale = np.asarray(scale, dtype=np.float32).astype(np.float64)
     O, I = codes.shape
     assert O % BLOCK == 0 and I % BLOCK == 0, "the oracle takes whole 128x128 blocks"
-    w = e4m3_decode(codes).reshape(O // BLOCK, BLOCK, I // BLOCK, BLOCK)
-    w = w * scale[:, None, :, None]
-    return w.reshape(O, I)
+    w = torch.take(_E4M3_T, torch.from_numpy(codes).long()).view(O // BLOCK, BLOCK, I // BLOCK, BLOCK)
+    w = w * torch.from_numpy(scale)[:, None, :, None]
+    return w.reshape(O, I).numpy()
 
 
 def quant_act(v):
@@ -301,8 +307,9 @@ def moe_forward(x, params, dims, tokens: Optional[Sequence[int]] = None,
     w1/s1/w3/s3/w2/s2 (routed, [E, ...]) and sh_w1/... (shared, [1, ...]).
     tokens: evaluate the expert part only for these tokens (routing is always
     computed for all).  idx: force this selection [T, K] (weights then come
-    from the oracle's own scores).  Returns routing, y (float64, unrounded)
-    and delta = bf16(y) for the evaluated tokens.
+    from the oracle's own scores).  routing: a gate() result to reuse.
+    Returns routing, y (float64, unrounded) and delta = bf16(y) for the
+    evaluated tokens.
     """
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape

@@ -1,0 +1,137 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, and rejects bad arguments on the host before it
+touches the device (each call below returns before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_ffn_bias_amd as moe
+from mixture_experts_ffn_bias_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moe.LIB_PATH), reason="libmoe.so not built")
+
+FULL = dict(d_model=7168, n_experts=256, n_groups=8, topk_groups=4, topk=8, inter=2048, route_scale=2.5)
+FAKE = 1 << 20          # a 256-byte aligned non-null address; never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(moe_[a-z_]+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_expected_entry_points():
+    assert declared_functions() == sorted(moe.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moe.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    assert moe.status_string(0) == "ok"
+    for c in (-1, -2, -3, -4, -5):
+        assert moe.status_string(c) not in ("ok", "unknown status")
+
+
+def dims(**kw):
+    d = dict(FULL)
+    d.update(kw)
+    return moe.make_dims(**d)
+
+
+def ws_size(**kw):
+    return moe.moe_workspace_size(dims(**kw), 64)
+
+
+def test_workspace_size_full_shape_decode():
+    n = ws_size()
+    assert n > 64 * 7168 * 9 * 2            # at least the bf16 expert-output rows
+    assert moe.moe_workspace_size(dims(), 0) >= 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(d_model=7000), dict(inter=2000), dict(n_experts=300), dict(n_experts=24, n_groups=8),
+    dict(topk=33, topk_groups=8), dict(n_groups=128, n_experts=256),
+])
+def test_unsupported_dims_have_no_workspace(bad):
+    assert ws_size(**bad) == 0
+
+
+@pytest.mark.parametrize("bad", [
+    dict(topk_groups=9), dict(topk=0), dict(n_experts=256, n_groups=7), dict(topk=130, topk_groups=4),
+    dict(route_scale=float("inf")), dict(d_model=-128),
+])
+def test_invalid_dims_are_rejected(bad):
+    rc = B.lib().moe_gate(ctypes.byref(dims(**bad)), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == -1
+
+
+def test_unsupported_dims_code():
+    rc = B.lib().moe_gate(ctypes.byref(dims(d_model=7000)), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+    assert rc == -2
+
+
+def test_null_dims_and_negative_tokens():
+    L = B.lib()
+    assert L.moe_gate(None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_gate(ctypes.byref(dims()), -1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+
+
+def test_zero_tokens_is_a_noop_everywhere():
+    L = B.lib()
+    d = ctypes.byref(dims())
+    assert L.moe_gate(d, 0, None, None, None, None, None, None, 0, None) == 0
+    assert L.moe_permute(d, 0, None, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.moe_grouped_ffn(d, 0, None, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.moe_combine(d, 0, None, None, None, None, 1, None, None) == 0
+    assert L.moe_forward(d, None, 0, None, None, None, None, None, 0, None) == 0
+    assert L.moe_add_rmsnorm(7168, 0, None, None, None, 1e-6, None, None) == 0
+
+
+def test_null_pointers_rejected():
+    L = B.lib()
+    d = ctypes.byref(dims())
+    assert L.moe_gate(d, 4, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_combine(d, 4, FAKE, FAKE, None, FAKE, 1, FAKE, None) == -1
+    ex = moe.moe_experts(FAKE, FAKE, None, FAKE, FAKE, FAKE)
+    assert L.moe_grouped_ffn(d, 4, ctypes.byref(ex), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_forward(d, None, 4, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == -1
+
+
+def test_workspace_too_small():
+    L = B.lib()
+    d = dims()
+    need = moe.moe_workspace_size(d, 64)
+    assert L.moe_gate(ctypes.byref(d), 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == -3
+    assert L.moe_gate(ctypes.byref(d), 64, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == -3
+
+
+def test_misaligned_pointers():
+    L = B.lib()
+    d = ctypes.byref(dims())
+    assert L.moe_gate(d, 4, FAKE + 2, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -4
+    assert L.moe_gate(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 16, 1 << 30, None) == -4
+    ex = moe.moe_experts(FAKE + 8, FAKE, FAKE, FAKE, FAKE, FAKE)
+    assert L.moe_grouped_ffn(d, 4, ctypes.byref(ex), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -4
+    assert L.moe_add_rmsnorm(7168, 4, FAKE + 2, FAKE, FAKE, 1e-6, FAKE, None) == -4
+
+
+def test_rmsnorm_argument_checks():
+    L = B.lib()
+    assert L.moe_add_rmsnorm(7000, 4, FAKE, FAKE, FAKE, 1e-6, FAKE, None) == -2
+    assert L.moe_add_rmsnorm(32768, 4, FAKE, FAKE, FAKE, 1e-6, FAKE, None) == -2
+    assert L.moe_add_rmsnorm(7168, 4, FAKE, FAKE, FAKE, -1.0, FAKE, None) == -1
+    assert L.moe_add_rmsnorm(0, 4, FAKE, FAKE, FAKE, 1e-6, FAKE, None) == -1
+
+
+def test_python_binding_raises_on_error_codes():
+    with pytest.raises(moe.MoeError) as ei:
+        moe.moe_gate(dims(topk_groups=9), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert ei.value.code == -1

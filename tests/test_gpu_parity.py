@@ -1,0 +1,387 @@
+"""GPU parity of every entry point of the C ABI against the CPU oracle.
+
+Inputs are seeded synthetic tensors from ``synth`` (shapes and value laws of
+the named workloads); expected values always come from ``oracle`` run on the
+same inputs.  Each entry point is tested alone on oracle-made inputs, then the
+fused forward end to end.  Full-shape (7168 x 256 experts) cases compare the
+routing of every token and the outputs of sampled tokens (the layer is
+token-wise, so a token's output depends on that token alone).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_ffn_bias_amd as moe
+import oracle
+import synth
+from _helpers import (HostView, assert_close, assert_rows_close, cdims, f64, metrics, routing_check,
+                      weights_check)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _say(msg):
+    print(f"[case] {msg}", flush=True)
+
+
+def _np_params(p):
+    return {k: v.cpu().numpy() for k, v in p.items()}
+
+
+@pytest.fixture(scope="module")
+def tiny_params():
+    return synth.make_block(synth.TINY, "normal:0.1", DEV, seed=0)
+
+
+def run_gate(dims, p, x):
+    T = x.shape[0]
+    cd = cdims(dims)
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device=DEV)
+    ws = moe.workspace(cd, T)
+    moe.moe_gate(cd, T, x, p["gate_w"], p["gate_b"], idx, w, ws)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy().astype(np.int64), w.cpu().numpy()
+
+
+def run_forward(dims, p, x):
+    layer = moe.MoELayer(cdims(dims), p)
+    T = x.shape[0]
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device=DEV)
+    delta = layer(x, idx=idx, w=w)
+    torch.cuda.synchronize()
+    return delta, idx.cpu().numpy().astype(np.int64), w.cpu().numpy()
+
+
+# ----------------------------------------------------------------------------
+# single entry points
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 37, 300])
+def test_activation_quant_bit_exact(T):
+    _say(f"moe_permute xq/xs T={T} d=512")
+    dims = synth.TINY
+    g = torch.Generator().manual_seed(T)
+    x = torch.randn((T, dims.d_model), generator=g) * torch.exp2(torch.empty((T, 4, 1)).uniform_(-20, 20, generator=g)
+                                                              ).repeat_interleave(128, 1).reshape(T, dims.d_model)
+    x[0, 128:256] = 0.0                      # an all-zero block
+    if T > 1:
+        x[1, :128] = 0.0
+        x[1, 5] = -3.0                       # a block with one non-zero element
+    xb = x.to(torch.bfloat16).to(DEV)
+    idx = torch.stack([torch.randperm(dims.n_experts, generator=g)[:dims.topk] for _ in range(T)]).int().to(DEV)
+    cd = cdims(dims)
+    K, E = dims.topk, dims.n_experts
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    row_token = torch.empty(T * K + T, dtype=torch.int32, device=DEV)
+    pair_row = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    xq = torch.empty((T, dims.d_model), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((T, dims.d_model // 128), dtype=torch.float32, device=DEV)
+    moe.moe_permute(cd, T, idx, xb, counts, offsets, row_token, pair_row, xq, xs, moe.workspace(cd, T))
+    torch.cuda.synchronize()
+    q_ref, s_ref = oracle.quant_act(f64(xb))
+    assert np.array_equal(xq.cpu().numpy(), q_ref)
+    assert np.array_equal(xs.cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 300])
+def test_gate_tiny(tiny_params, T):
+    _say(f"moe_gate tiny T={T}")
+    dims = synth.TINY
+    x = synth.make_x(dims, T, DEV, seed=10 + T)
+    gi, gw = run_gate(dims, tiny_params, x)
+    p = _np_params(tiny_params)
+    r = oracle.gate(f64(x), p["gate_w"], p["gate_b"], dims)
+    same, ndiff = routing_check(gi, r, dims)
+    assert ndiff == 0
+    weights_check(gi, gw, r, same)
+    # descending biased score on the GPU side too
+    for t in range(T):
+        b = r["b"][t, gi[t]]
+        assert np.all(np.diff(b) <= 1e-6)
+
+
+def test_gate_exact_ties_go_to_the_lower_index():
+    _say("moe_gate hand-built ties")
+    # x = 0: every score is exactly 0.5, so biased scores are 0.5 + bias (multiples of 1/64)
+    dims = synth.Dims(d_model=128, n_experts=16, n_groups=8, topk_groups=4, topk=4, inter=128)
+    bias = torch.tensor([16, 0, 20, -20, 12, 12, 6, 3, 12, 12, -30, -30, 0, 0, 5, 5], dtype=torch.float32) / 64
+    p = {"gate_w": torch.ones((16, 128), device=DEV), "gate_b": bias.to(DEV)}
+    x = torch.zeros((3, 128), dtype=torch.bfloat16, device=DEV)
+    gi, gw = run_gate(dims, p, x)
+    r = oracle.gate(np.zeros((3, 128)), np.ones((16, 128), np.float32), bias.numpy(), dims)
+    assert np.array_equal(gi, r["idx"])
+    assert np.allclose(gw, 2.5 / 4)
+
+
+@pytest.mark.parametrize("T,E,K", [(64, 16, 4), (300, 16, 4), (1000, 256, 8), (5000, 256, 8)])
+def test_permute_exact(T, E, K):
+    _say(f"moe_permute T={T} E={E} K={K}")
+    dims = synth.Dims(d_model=256, n_experts=E, n_groups=E // 4, topk_groups=E // 4, topk=K, inter=128)
+    rng = np.random.default_rng(T)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)])
+    if T >= 1000:
+        idx[: T // 2, 0] = 7                       # one hot expert spanning many chunks
+        for t in range(T // 2):
+            row = idx[t]
+            dup = np.flatnonzero(row[1:] == 7)
+            if dup.size:
+                row[1 + dup[0]] = [e for e in range(E) if e not in row][0]
+    x = torch.zeros((T, 256), dtype=torch.bfloat16, device=DEV)
+    cd = cdims(dims)
+    counts = torch.empty(E, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(E + 1, dtype=torch.int32, device=DEV)
+    row_token = torch.empty(T * K + T, dtype=torch.int32, device=DEV)
+    pair_row = torch.empty((T, K), dtype=torch.int32, device=DEV)
+    xq = torch.empty((T, 256), dtype=torch.uint8, device=DEV)
+    xs = torch.empty((T, 2), dtype=torch.float32, device=DEV)
+    moe.moe_permute(cd, T, torch.from_numpy(idx).int().to(DEV), x, counts, offsets, row_token, pair_row, xq, xs,
+                    moe.workspace(cd, T))
+    torch.cuda.synchronize()
+    ref = oracle.permute(idx, E)
+    assert np.array_equal(counts.cpu().numpy(), ref["counts"])
+    assert np.array_equal(offsets.cpu().numpy(), ref["offsets"])
+    rt = row_token.cpu().numpy()
+    assert np.array_equal(rt[: T * K], ref["row_token"])
+    assert np.array_equal(rt[T * K:], np.arange(T))
+    assert np.array_equal(pair_row.cpu().numpy(), ref["pair_row"])
+
+
+def _ffn_with_oracle_routing(dims, p, x, with_shared=True):
+    """GPU grouped FFN fed with the oracle's routing, permutation and quantised x."""
+    T, K, E, d = x.shape[0], dims.topk, dims.n_experts, dims.d_model
+    pn = _np_params(p)
+    xv = f64(x)
+    r = oracle.gate(xv, pn["gate_w"], pn["gate_b"], dims)
+    perm = oracle.permute(r["idx"], E)
+    xq, xs = oracle.quant_act(xv)
+    rows_tok = np.concatenate([perm["row_token"], np.arange(T)]).astype(np.int32)
+    cd = cdims(dims)
+    out = torch.zeros((T * K + T, d), dtype=torch.bfloat16, device=DEV)
+    routed = moe.experts_struct(*(p[k] for k in ("w1", "w3", "w2", "s1", "s3", "s2")))
+    shared = moe.experts_struct(*(p["sh_" + k] for k in ("w1", "w3", "w2", "s1", "s3", "s2"))) if with_shared else None
+    moe.moe_grouped_ffn(cd, T, routed, shared, torch.from_numpy(perm["offsets"]).int().to(DEV),
+                        torch.from_numpy(rows_tok).to(DEV), torch.from_numpy(xq).to(DEV),
+                        torch.from_numpy(xs).to(DEV), out, moe.workspace(cd, T))
+    torch.cuda.synchronize()
+    return out, r, perm, pn, xv
+
+
+@pytest.mark.parametrize("T", [37, 300])
+def test_grouped_ffn_forced_routing_tiny(tiny_params, T):
+    _say(f"moe_grouped_ffn tiny T={T}")
+    dims = synth.TINY
+    x = synth.make_x(dims, T, DEV, seed=20 + T)
+    out, r, perm, pn, xv = _ffn_with_oracle_routing(dims, tiny_params, x)
+    got = f64(out)
+    off = perm["offsets"]
+    ref = np.zeros_like(got)
+    for e in range(dims.n_experts):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size:
+            ref[rows] = oracle.expert_ffn(xv[perm["row_token"][rows]], pn["w1"][e], pn["s1"][e], pn["w3"][e],
+                                          pn["s3"][e], pn["w2"][e], pn["s2"][e])
+    ref[T * dims.topk:] = oracle.expert_ffn(xv, pn["sh_w1"][0], pn["sh_s1"][0], pn["sh_w3"][0], pn["sh_s3"][0],
+                                            pn["sh_w2"][0], pn["sh_s2"][0])
+    assert_rows_close(got, ref, f"grouped_ffn tiny T={T}")
+
+
+def test_grouped_ffn_without_shared_leaves_shared_rows(tiny_params):
+    _say("moe_grouped_ffn shared=NULL")
+    dims = synth.TINY
+    x = synth.make_x(dims, 20, DEV, seed=3)
+    out, *_ = _ffn_with_oracle_routing(dims, tiny_params, x, with_shared=False)
+    assert torch.all(out[20 * dims.topk:] == 0)
+
+
+def test_combine_with_oracle_rows():
+    _say("moe_combine oracle rows")
+    dims = synth.Dims(d_model=1024, n_experts=64, n_groups=8, topk_groups=4, topk=8, inter=128)
+    T, K, d = 50, dims.topk, dims.d_model
+    rng = np.random.default_rng(5)
+    idx = np.stack([rng.choice(dims.n_experts, K, replace=False) for _ in range(T)])
+    w = rng.uniform(0.1, 1.0, (T, K))
+    w = (w / w.sum(1, keepdims=True) * 2.5).astype(np.float32).astype(np.float64)
+    perm = oracle.permute(idx, dims.n_experts)
+    rows = oracle.bf16_round(rng.standard_normal((T * K + T, d)) * 0.05)
+    y = np.zeros((T, d))
+    for t in range(T):                                     # ascending expert order, then shared
+        for k in np.argsort(idx[t]):
+            y[t] += w[t, k] * rows[perm["pair_row"][t, k]]
+        y[t] += rows[T * K + t]
+    delta = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
+    moe.moe_combine(cdims(dims), T, torch.from_numpy(idx).int().to(DEV), torch.from_numpy(w).float().to(DEV),
+                    torch.from_numpy(perm["pair_row"]).int().to(DEV),
+                    torch.from_numpy(rows).to(torch.bfloat16).to(DEV), True, delta)
+    torch.cuda.synchronize()
+    got = f64(delta)
+    # fp32 accumulation + one final bf16 rounding: within one bf16 ulp of the exact sum
+    assert np.all(np.abs(got - y) <= np.abs(y) * 2.0 ** -8 + 1e-6)
+
+
+@pytest.mark.parametrize("T", [1, 37, 4096])
+def test_add_rmsnorm(T):
+    _say(f"moe_add_rmsnorm T={T}")
+    d = 7168
+    g = torch.Generator(device=DEV).manual_seed(T)
+    x = torch.randn((T, d), generator=g, device=DEV).to(torch.bfloat16)
+    res = (torch.randn((T, d), generator=g, device=DEV) * 4).to(torch.bfloat16)
+    gain = 1 + 0.02 * torch.randn(d, generator=g, device=DEV)
+    hn_ref, res_ref = oracle.add_rmsnorm(f64(x), f64(res), gain.cpu().numpy())
+    out = torch.empty_like(x)
+    moe.moe_add_rmsnorm(d, T, x, res, gain, 1e-6, out)
+    torch.cuda.synchronize()
+    assert np.array_equal(f64(res), res_ref)                    # new residual: bit-exact
+    got = f64(out)
+    ulp = np.abs(hn_ref) * 2.0 ** -7
+    assert np.all(np.abs(got - hn_ref) <= ulp + 1e-30)          # within one bf16 ulp
+    assert np.mean(got == hn_ref) > 0.99
+
+
+def test_add_rmsnorm_in_place_output():
+    _say("moe_add_rmsnorm out aliases x")
+    d, T = 512, 9
+    x = torch.randn((T, d), device=DEV).to(torch.bfloat16)
+    res = torch.randn((T, d), device=DEV).to(torch.bfloat16)
+    gain = torch.ones(d, device=DEV)
+    x2, res2 = x.clone(), res.clone()
+    out = torch.empty_like(x)
+    moe.moe_add_rmsnorm(d, T, x, res, gain, 1e-6, out)
+    moe.moe_add_rmsnorm(d, T, x2, res2, gain, 1e-6, x2)
+    torch.cuda.synchronize()
+    assert torch.equal(out, x2) and torch.equal(res, res2)
+
+
+# ----------------------------------------------------------------------------
+# fused forward, tiny shape
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T", [1, 37, 64, 1000])
+def test_forward_tiny(tiny_params, T):
+    _say(f"moe_forward tiny T={T}")
+    dims = synth.TINY
+    x = synth.make_x(dims, T, DEV, seed=30 + T)
+    delta, gi, gw = run_forward(dims, tiny_params, x)
+    ref = oracle.moe_forward(f64(x), _np_params(tiny_params), dims)
+    same, _ = routing_check(gi, ref["routing"], dims)
+    weights_check(gi, gw, ref["routing"], same)
+    assert_close(f64(delta)[same], ref["y"][same], f"forward tiny T={T}")
+
+
+def test_forward_is_deterministic(tiny_params):
+    _say("moe_forward determinism")
+    dims = synth.TINY
+    x = synth.make_x(dims, 1000, DEV, seed=4)
+    a, *_ = run_forward(dims, tiny_params, x)
+    b, *_ = run_forward(dims, tiny_params, x)
+    assert torch.equal(a, b)
+
+
+def test_forward_zero_tokens(tiny_params):
+    _say("moe_forward T=0")
+    layer = moe.MoELayer(cdims(synth.TINY), tiny_params)
+    out = layer(torch.empty((0, synth.TINY.d_model), dtype=torch.bfloat16, device=DEV))
+    assert out.shape == (0, synth.TINY.d_model)
+
+
+def test_forward_all_tokens_on_one_group(tiny_params):
+    _say("moe_forward hot group (multi-tile experts)")
+    dims = synth.TINY
+    p = dict(tiny_params)
+    bias = torch.full((dims.n_experts,), -5.0, device=DEV)
+    bias[:4] = 5.0                                   # group 0 wins for every token
+    bias[4:8] = 4.0                                  # group 1 second
+    p["gate_b"] = bias
+    T = 300                                          # experts 0..7 get ~300 rows: three 128-row tiles
+    x = synth.make_x(dims, T, DEV, seed=6)
+    delta, gi, _ = run_forward(dims, p, x)
+    assert set(np.unique(gi).tolist()) <= set(range(8))
+    ref = oracle.moe_forward(f64(x), _np_params(p), dims)
+    same, _ = routing_check(gi, ref["routing"], dims)
+    assert_close(f64(delta)[same], ref["y"][same], "forward hot group")
+
+
+def test_forward_nan_token_is_contained(tiny_params):
+    _say("moe_forward NaN input")
+    dims = synth.TINY
+    x = synth.make_x(dims, 40, DEV, seed=7)
+    clean, gi_clean, _ = run_forward(dims, tiny_params, x)
+    xn = x.clone()
+    xn[3, 17] = float("nan")
+    dirty, gi, _ = run_forward(dims, tiny_params, xn)
+    assert np.all((gi >= 0) & (gi < dims.n_experts))
+    for t in range(40):
+        assert len(set(gi[t].tolist())) == dims.topk
+    keep = [t for t in range(40) if t != 3]
+    assert torch.equal(dirty[keep], clean[keep])
+    assert np.array_equal(gi[keep], gi_clean[keep])
+
+
+# ----------------------------------------------------------------------------
+# fused forward, full shape (d 7168, 256 experts, top-8 of 4 groups)
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def full_params():
+    _say("generating full-shape weights on the GPU")
+    p = synth.make_block(synth.FULL, "normal:0.01", DEV, seed=1)
+    torch.cuda.synchronize()
+    return p
+
+
+def _sample_tokens(r, T, K, n_random, seed, tile=128):
+    """Random tokens plus tokens that sit at 128-row tile edges of the busiest experts."""
+    rng = np.random.default_rng(seed)
+    pick = set(rng.choice(T, min(n_random, T), replace=False).tolist())
+    perm = oracle.permute(r["idx"], r["idx"].max() + 1)
+    counts = perm["counts"]
+    for e in np.argsort(-counts)[:2]:
+        lo, hi = perm["offsets"][e], perm["offsets"][e + 1]
+        for pos in (lo, hi - 1, lo + tile - 1, lo + tile):
+            if lo <= pos < hi:
+                pick.add(int(perm["row_token"][pos]))
+    return np.array(sorted(pick))
+
+
+def _full_case(params, bias, T, seed, n_random):
+    dims = synth.FULL
+    p = dict(params)
+    p["gate_b"] = bias
+    x = synth.make_x(dims, T, DEV, seed=seed)
+    delta, gi, gw = run_forward(dims, p, x)
+    hv = HostView(p)
+    xv = f64(x)
+    r = oracle.gate(xv, hv["gate_w"], hv["gate_b"], dims)
+    same, ndiff = routing_check(gi, r, dims)
+    print(f"[parity] T={T}: {ndiff} near-tie tokens route differently", flush=True)
+    weights_check(gi, gw, r, same)
+    tok = _sample_tokens(r, T, dims.topk, n_random, seed)
+    tok = tok[same[tok]]
+    ref = oracle.moe_forward(xv, hv, dims, tokens=tok, routing=r)
+    return assert_close(f64(delta)[tok], ref["y"], f"forward full T={T} ({tok.size} sampled tokens)")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_forward_full_decode(full_params):
+    _say("moe_forward full shape T=64 (decode)")
+    bias = 0.01 * torch.randn(256, generator=torch.Generator(device=DEV).manual_seed(11), device=DEV)
+    _full_case(full_params, bias, 64, seed=101, n_random=6)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_forward_full_prefill(full_params):
+    _say("moe_forward full shape T=4096 bias 0 (prefill)")
+    _full_case(full_params, torch.zeros(256, device=DEV), 4096, seed=102, n_random=4)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_forward_full_skewed(full_params):
+    _say("moe_forward full shape T=16384 Zipf bias (skewed)")
+    bias = synth.gate_bias(synth.FULL, "zipf", DEV, seed=3, tag=1002)
+    _full_case(full_params, bias, 16384, seed=103, n_random=3)
