@@ -1,0 +1,298 @@
+"""Benchmark of the DeepSeek-V3.2-Exp MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|stack4|tiny]
+
+A step is one pass of the whole layer (router, permutation, grouped expert
+FFN, combine; for the stacked workload four blocks of fused residual-add
+RMSNorm + layer) over one batch of synthetic, seeded inputs that are resident
+in HBM before timing starts.  Prints one JSON line with tokens/s, the
+roofline position of the dominant kernel (timed with HIP events on the
+library's stream inside the timed region) and the CPU oracle's throughput on a
+bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+STAGES = ("gate", "permute", "ffn_up", "ffn_down", "combine")
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime already loaded by torch."""
+
+    def __init__(self):
+        path = None
+        for m in re.findall(r"(/\S*libamdhip64\S*)", open("/proc/self/maps").read()):
+            path = m
+            break
+        self.hip = ctypes.CDLL(path or "libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            ev = ctypes.c_void_p()
+            rc = self.hip.hipEventCreate(ctypes.byref(ev))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+            out.append(ev.value)
+        self.made.extend(out)
+        return out
+
+    def ms(self, a, b) -> float:
+        v = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(v), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(v.value)
+
+    def close(self):
+        for e in self.made:
+            self.hip.hipEventDestroy(ctypes.c_void_p(e))
+        self.made = []
+
+
+def algorithmic_work(dims, T, touched):
+    """Bytes and FLOPs each kernel must move / compute (implementation buffers excluded).
+
+    touched: number of routed experts with at least one row (the shared expert comes on top).
+    """
+    d, I, K = dims.d_model, dims.inter, dims.topk
+    R = T * K + T                                  # routed rows + shared rows
+    ne = touched + 1
+    up_w = 2 * I * d + 2 * (I // 128) * (d // 128) * 4
+    dn_w = I * d + (d // 128) * (I // 128) * 4
+    up_bytes = ne * up_w + T * d + T * (d // 128) * 4 + R * (I + (I // 128) * 4)
+    dn_bytes = ne * dn_w + R * (I + (I // 128) * 4) + R * d * 2
+    return {
+        "ffn_up": {"bytes": up_bytes, "flops": 2 * R * d * 2 * I},
+        "ffn_down": {"bytes": dn_bytes, "flops": 2 * R * I * d},
+        "layer_bytes": ne * (up_w + dn_w) + dims.n_experts * d * 4 + dims.n_experts * 4 + 2 * T * d * 2,
+        "layer_flops": 2 * R * 3 * d * I,
+    }
+
+
+def cpu_baseline(x, params, dims, budget_s, threads, residual=None, gain=None, seed=0):
+    """The oracle on host cores over a bounded, seeded sample of tokens.
+
+    Tokens are taken two at a time in a seeded random order until budget_s
+    seconds of oracle work have been spent.  The weights of the experts a
+    batch needs are copied to host memory before its timed call.  With a
+    residual and gain, each timed call also includes the fused residual-add
+    RMSNorm in front of the layer.
+    """
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+
+    import oracle
+
+    torch.set_num_threads(threads)
+    rng = np.random.default_rng(seed)
+    T = x.shape[0]
+    order = rng.permutation(T)
+    names = ("w1", "s1", "w3", "s3", "w2", "s2")
+    xv_all = x.float().cpu().numpy().astype(np.float64)
+    rv_all = residual.float().cpu().numpy().astype(np.float64) if residual is not None else None
+    gv = gain.cpu().numpy() if gain is not None else None
+    host = {"gate_w": params["gate_w"].cpu().numpy(), "gate_b": params["gate_b"].cpu().numpy()}
+    for n in names:
+        host["sh_" + n] = params["sh_" + n].cpu().numpy()
+    cache = {}
+
+    class Rows:
+        def __init__(self, n):
+            self.n = n
+
+        def __getitem__(self, e):
+            if (self.n, e) not in cache:           # only reached if a batch needs an unfetched expert
+                cache[(self.n, e)] = params[self.n][e].cpu().numpy()
+            return cache[(self.n, e)]
+
+    for n in names:
+        host[n] = Rows(n)
+    done, elapsed, i = 0, 0.0, 0
+    with threadpool_limits(limits=threads):
+        while i < T and elapsed < budget_s:
+            batch = order[i:i + 2]
+            i += len(batch)
+            xb = xv_all[batch]
+            if rv_all is not None:
+                xin, _ = oracle.add_rmsnorm(xb, rv_all[batch], gv)
+            else:
+                xin = xb
+            sel = oracle.gate(xin, host["gate_w"], host["gate_b"], dims)["idx"]
+            if len(cache) > 6 * 300:
+                cache.clear()
+            for e in set(sel.ravel().tolist()):     # untimed: host copies of the needed weights
+                for n in names:
+                    host[n][e]
+            t0 = time.perf_counter()
+            if rv_all is not None:
+                xin, _ = oracle.add_rmsnorm(xb, rv_all[batch], gv)
+            oracle.moe_forward(xin, host, dims)
+            elapsed += time.perf_counter() - t0
+            done += len(batch)
+    what = "fused residual-add RMSNorm + layer" if residual is not None else "layer"
+    return {"value": round(done / elapsed, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {T} tokens (seeded random order, 2 per call), {what}: router + the experts "
+                      f"the sample selects + shared expert, float64, {elapsed:.1f} s of oracle time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skewed", "stack4"])
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_bias_amd as moe
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    wl = synth.WORKLOADS[args.workload]
+    dims = wl.dims
+    data = synth.make_workload(args.workload, device=dev)
+    T = data["tokens"]
+    cd = moe.make_dims(dims.d_model, dims.n_experts, dims.n_groups, dims.topk_groups, dims.topk, dims.inter,
+                       dims.route_scale)
+    layers = [moe.MoELayer(cd, p) for p in data["blocks"]]
+    nb = len(layers)
+    x0 = data["x"]
+    ws = layers[0].workspace(T)
+    stream = torch.cuda.current_stream()
+    delta = torch.empty_like(x0)
+    idx = [torch.empty((T, dims.topk), dtype=torch.int32, device=dev) for _ in range(nb)]
+    w = [torch.empty((T, dims.topk), dtype=torch.float32, device=dev) for _ in range(nb)]
+    if nb > 1:
+        res0 = data["residual"]
+        res = torch.empty_like(res0)
+        h = torch.empty_like(x0)
+        cur = torch.empty_like(x0)
+    hev = HipEvents()
+    torch.cuda.synchronize()
+
+    def step(events=None):
+        if nb == 1:
+            if events is None:
+                moe.moe_forward(cd, layers[0].weights, T, x0, delta, idx[0], w[0], ws, stream)
+            else:
+                moe.moe_forward_timed(cd, layers[0].weights, T, x0, delta, idx[0], w[0], ws, events[0], stream)
+            return
+        res.copy_(res0)
+        src = x0
+        for b in range(nb):
+            moe.moe_add_rmsnorm(dims.d_model, T, src, res, data["gains"][b], 1e-6, h, stream)
+            out = delta if b == nb - 1 else cur
+            if events is None:
+                moe.moe_forward(cd, layers[b].weights, T, h, out, idx[b], w[b], ws, stream)
+            else:
+                moe.moe_forward_timed(cd, layers[b].weights, T, h, out, idx[b], w[b], ws, events[b], stream)
+            src = out
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [[hev.create(moe.MOE_FORWARD_EVENTS) for _ in range(nb)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+
+    stage_ms = {s: 0.0 for s in STAGES}
+    for k in range(K):
+        for b in range(nb):
+            e = evs[k][b]
+            for i, s in enumerate(STAGES):
+                stage_ms[s] += hev.ms(e[i], e[i + 1])
+    launches = K * nb
+    stage_avg = {s: v / launches for s, v in stage_ms.items()}
+    hev.close()
+
+    # algorithmic work of the dominant kernel (per launch; blocks of the stack are alike)
+    counts = [np.bincount(i.cpu().numpy().ravel(), minlength=dims.n_experts) for i in idx]
+    touched = [int((c > 0).sum()) for c in counts]
+    work = [algorithmic_work(dims, T, t) for t in touched]
+    dom = max(("ffn_up", "ffn_down"), key=lambda s: stage_avg[s])
+    dur = stage_avg[dom] * 1e-3
+    bytes_per = sum(wk[dom]["bytes"] for wk in work) / nb
+    flops_per = sum(wk[dom]["flops"] for wk in work) / nb
+    gbs = bytes_per / dur / 1e9
+    tfs = flops_per / dur / 1e12
+    if gbs / HBM_PEAK_GBS >= tfs / BF16_MFMA_PEAK_TFLOPS:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4)}
+    roof.update({"kernel": dom, "traffic": None, "launch_ms": round(stage_avg[dom], 4),
+                 "alg_bytes": int(bytes_per), "alg_flops": int(flops_per)})
+
+    tokens = T * K
+    layer_bytes = sum(wk["layer_bytes"] for wk in work)
+    step_s = wall / K
+    out = {
+        "metric": "MoE layer tokens/s (d7168,256e,top8) + % of fp8 MFMA / HBM roofline",
+        "value": round(tokens / wall, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "blocks": nb, "d_model": dims.d_model,
+                   "experts": dims.n_experts, "groups": dims.n_groups, "topk_groups": dims.topk_groups,
+                   "topk": dims.topk, "inter": dims.inter, "weights": "e4m3 + fp32 128x128 block scales",
+                   "touched_experts": touched},
+        "roofline": roof,
+        "layer": {"alg_bytes_per_step": int(layer_bytes), "hbm_GBps": round(layer_bytes / step_s / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+                  "stage_ms": {s: round(v, 4) for s, v in stage_avg.items()}},
+    }
+    if not args.no_cpu_baseline:
+        threads = max(1, min(16, os.cpu_count() or 1))
+        if nb > 1:
+            out["cpu_baseline"] = cpu_baseline(x0, data["blocks"][0], dims, args.cpu_budget, threads,
+                                               residual=data["residual"], gain=data["gains"][0])
+            out["cpu_baseline"]["sample"] += "; first block of the stack, so tokens/s per block"
+        else:
+            out["cpu_baseline"] = cpu_baseline(x0, data["blocks"][0], dims, args.cpu_budget, threads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -151,6 +151,19 @@ int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens
                 const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Number of events moe_forward_timed records. */
+#define MOE_FORWARD_EVENTS 6
+
+/* moe_forward that also records stage_events[0..5] (hipEvent_t handles the
+ * caller created, host array) on `stream`: before the gate, before the
+ * permutation, before the up-projection (w1/w3, SwiGLU, h quantisation),
+ * before the down-projection (w2), before the combine, and after it.  For
+ * per-kernel timing; the computation is identical to moe_forward. */
+int moe_forward_timed(const moe_dims* dims, const moe_weights* weights, int64_t tokens,
+                      const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
+                      void* workspace, size_t workspace_bytes, void* stream,
+                      void* const* stage_events);
+
 /* Fused residual add + RMSNorm ("MoE update", rmsnorm excerpt, residual branch):
  *   r = float(x) + float(residual);  residual <- bf16(r);
  *   out = bf16(gain * r * rsqrt(mean(r^2) + eps))   (fp32 arithmetic)

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK = 0
 SYMBOLS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-           "moe_add_rmsnorm", "moe_status_string")
+           "moe_forward_timed", "moe_add_rmsnorm", "moe_status_string")
+MOE_FORWARD_EVENTS = 6
 
 
 class MoeError(RuntimeError):
@@ -62,8 +63,11 @@ def lib() -> ctypes.CDLL:
                                       vp, vp, vp, sz, vp]
         L.moe_combine.argtypes = [dp, i64, vp, vp, vp, vp, i32, vp, vp]
         L.moe_forward.argtypes = [dp, ctypes.POINTER(moe_weights), i64, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_forward_timed.argtypes = [dp, ctypes.POINTER(moe_weights), i64, vp, vp, vp, vp, vp, sz, vp,
+                                        ctypes.POINTER(ctypes.c_void_p)]
         L.moe_add_rmsnorm.argtypes = [i32, i64, vp, vp, vp, ctypes.c_float, vp, vp]
-        for n in ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_add_rmsnorm"):
+        for n in ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
+                  "moe_add_rmsnorm"):
             getattr(L, n).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -143,6 +147,14 @@ def moe_forward(dims, weights: moe_weights, tokens, x, delta, idx_out, w_out, ws
     _check(lib().moe_forward(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta), _p(idx_out),
                              _p(w_out), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_timed(dims, weights: moe_weights, tokens, x, delta, idx_out, w_out, ws, events, stream=None):
+    """events: MOE_FORWARD_EVENTS hipEvent_t handles (ints), e.g. from HipEvents."""
+    arr = (ctypes.c_void_p * MOE_FORWARD_EVENTS)(*events)
+    _check(lib().moe_forward_timed(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta),
+                                   _p(idx_out), _p(w_out), _p(ws), ws.numel() if ws is not None else 0,
+                                   _stream(stream), arr), "moe_forward_timed")
 
 
 def moe_add_rmsnorm(d, tokens, x, residual, gain, eps, out, stream=None):

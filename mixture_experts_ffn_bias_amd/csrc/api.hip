@@ -181,9 +181,16 @@ int moe_combine(const moe_dims* dims, int64_t tokens, const int32_t* idx, const 
                                    d.d_model, delta, (hipStream_t)stream));
 }
 
-int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
-                uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
-                void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The fused forward.  ev: NULL or MOE_FORWARD_EVENTS events, recorded before
+// the gate, before the permutation, before the up-projection, before the
+// down-projection, before the combine and after it.
+int forward_impl(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
+                 uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                 hipStream_t s, hipEvent_t* ev) {
   MOE_TRY(check_dims(dims));
   MOE_TRY(check_tokens(*dims, tokens));
   if (tokens == 0) return MOE_OK;
@@ -197,7 +204,6 @@ int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens
   if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
   if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
   const moe_dims& d = *dims;
-  const hipStream_t s = (hipStream_t)stream;
   const int T = (int)tokens;
   int32_t* idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
   float* w = w_out ? w_out : at<float>(workspace, L.w);
@@ -207,17 +213,46 @@ int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens
   uint8_t* xq = at<uint8_t>(workspace, L.xq);
   float* xs = at<float>(workspace, L.xs);
   uint16_t* rows = at<uint16_t>(workspace, L.rows);
+  if (ev) (void)hipEventRecord(ev[0], s);
   MOE_TRY(hip_status(launch_gate(x, weights->gate_w, weights->gate_b, T, d.d_model, d.n_experts, d.n_groups,
                                  d.topk_groups, d.topk, d.route_scale, at<float>(workspace, L.zpart),
                                  gate_ksplit(tokens, d.d_model, d.n_experts), idx, w, s)));
+  if (ev) (void)hipEventRecord(ev[1], s);
   MOE_TRY(hip_status(launch_permute(idx, x, T, d.d_model, d.n_experts, d.topk, at<int32_t>(workspace, L.chunk_cnt),
                                     at<int32_t>(workspace, L.chunk_off), at<int32_t>(workspace, L.counts), offsets,
                                     row_token, pair_row, xq, xs, s)));
   const ExpertPtrs rp = ptrs(weights->routed), sp = ptrs(weights->shared);
   MOE_TRY(hip_status(launch_ffn(rp, &sp, T, d.d_model, d.inter, d.n_experts, d.topk, offsets, row_token, xq, xs,
                                 at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
-                                at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), rows, s)));
-  return hip_status(launch_combine(idx, w, pair_row, rows, 1, T, d.topk, d.n_experts, d.d_model, delta, s));
+                                at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), rows, s,
+                                ev ? ev + 2 : nullptr)));
+  const int st = hip_status(launch_combine(idx, w, pair_row, rows, 1, T, d.topk, d.n_experts, d.d_model, delta, s));
+  if (ev) (void)hipEventRecord(ev[5], s);
+  return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
+                uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                void* stream) {
+  return forward_impl(dims, weights, tokens, x, delta, idx_out, w_out, workspace, workspace_bytes,
+                      (hipStream_t)stream, nullptr);
+}
+
+int moe_forward_timed(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
+                      uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                      void* stream, void* const* stage_events) {
+  if (!stage_events) return MOE_ERR_INVALID_ARG;
+  hipEvent_t ev[MOE_FORWARD_EVENTS];
+  for (int i = 0; i < MOE_FORWARD_EVENTS; ++i) {
+    if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+    ev[i] = (hipEvent_t)stage_events[i];
+  }
+  return forward_impl(dims, weights, tokens, x, delta, idx_out, w_out, workspace, workspace_bytes,
+                      (hipStream_t)stream, ev);
 }
 
 int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* residual, const float* gain, float eps,

@@ -218,13 +218,17 @@ __global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
 }
 
 template <int MT>
-hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s) {
+hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
   const int64_t g1 = max_tiles * (a.I / BLK), g2 = max_tiles * (a.d / BLK);
+  if (ev) (void)hipEventRecord(ev[0], s);
   hipLaunchKernelGGL(ffn_up_kernel<MT>, dim3((unsigned)g1), dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (ev) (void)hipEventRecord(ev[1], s);
   hipLaunchKernelGGL(ffn_down_kernel<MT>, dim3((unsigned)g2), dim3(512), 0, s, a);
-  return hipGetLastError();
+  err = hipGetLastError();
+  if (ev) (void)hipEventRecord(ev[2], s);
+  return err;
 }
 
 }  // namespace
@@ -242,7 +246,8 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows) {
 
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E, int K,
                       const int32_t* offsets, const int32_t* row_token, const uint8_t* xq, const float* xs,
-                      int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs, uint16_t* out, hipStream_t s) {
+                      int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs, uint16_t* out, hipStream_t s,
+                      hipEvent_t* ev) {
   const int NT = ffn_tile_rows(T);
   const int64_t max_tiles = ffn_max_tiles(T, K, E, NT);
   const int nsh = shared ? (T + NT - 1) / NT : 0;
@@ -267,10 +272,10 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
   a.hs = hs;
   a.out = out;
   switch (NT) {
-    case 16: return launch_gemms<1>(a, max_tiles, s);
-    case 32: return launch_gemms<2>(a, max_tiles, s);
-    case 64: return launch_gemms<4>(a, max_tiles, s);
-    default: return launch_gemms<8>(a, max_tiles, s);
+    case 16: return launch_gemms<1>(a, max_tiles, s, ev);
+    case 32: return launch_gemms<2>(a, max_tiles, s, ev);
+    case 64: return launch_gemms<4>(a, max_tiles, s, ev);
+    default: return launch_gemms<8>(a, max_tiles, s, ev);
   }
 }
 

@@ -33,10 +33,12 @@ hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, i
 // ffn.hip
 int ffn_tile_rows(int64_t T);                       // rows per FFN tile for this token count
 int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
+// ev: NULL, or three events recorded before the up-projection, before the
+// down-projection and after it (the tile plan precedes ev[0]).
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E,
                       int K, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
                       const float* xs, int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs,
-                      uint16_t* out, hipStream_t s);
+                      uint16_t* out, hipStream_t s, hipEvent_t* ev = nullptr);
 
 // combine.hip
 hipError_t launch_combine(const int32_t* idx, const float* w, const int32_t* pair_row, const uint16_t* rows,
