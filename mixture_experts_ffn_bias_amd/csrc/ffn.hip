@@ -21,6 +21,9 @@ namespace moe {
 
 namespace {
 
+constexpr int STREAM_DEPTH = 4;          // K-blocks in flight per wave in the streaming kernels
+constexpr int64_t STREAM_MAX_TOKENS = 128;
+
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // One block of 256 threads.  tiles[i] = {expert, first row, rows, 0}; the
@@ -74,9 +77,270 @@ struct FfnArgs {
   uint16_t* out;
 };
 
-// grid = max_tiles * (I/128), block = 512 (8 waves)
-template <int MT>
-__global__ __launch_bounds__(512) void ffn_up_kernel(FfnArgs a) {
+// ---------------------------------------------------------------------------
+// Streaming variants for small batches (every tile <= 16 rows): the weights
+// are read once from HBM and dominate the traffic, so each wave keeps P
+// K-blocks of raw e4m3 fragments (weights, activations, activation scales)
+// in flight in a register ring and issues the loads for block kb+P before it
+// decodes and multiplies block kb.
+// ---------------------------------------------------------------------------
+
+template <int P>
+__global__ __launch_bounds__(512) void ffn_up_stream_kernel(FfnArgs a) {
+  const int nib = a.I / BLK, nkb = a.d / BLK;
+  const int tile = blockIdx.x / nib, ib = blockIdx.x - tile * nib;
+  if (tile >= *a.n_tiles) return;  // uniform for the whole block, before any barrier
+  const int4 td = a.tiles[tile];
+  const int e = td.x, row0 = td.y, nrows = td.z;
+  const bool sh = e >= a.E;
+  const ExpertPtrs& Pp = sh ? a.shared : a.routed;
+  const size_t eo = sh ? 0 : (size_t)e;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int o = ib * BLK + 16 * wave + r;
+  const uint8_t* a1 = Pp.w1 + (eo * a.I + o) * (size_t)a.d;
+  const uint8_t* a3 = Pp.w3 + (eo * a.I + o) * (size_t)a.d;
+  const float* s1 = Pp.s1 + (eo * nib + ib) * nkb;
+  const float* s3 = Pp.s3 + (eo * nib + ib) * nkb;
+  const int tok = clampi(a.row_token[row0 + min(r, nrows - 1)], 0, a.T - 1);
+  const uint8_t* bq = a.xq + (size_t)tok * a.d;
+  const float* bs = a.xs + (size_t)tok * nkb;
+
+  v8i ra1[P], ra3[P], rb[P];
+  float rx[P];
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    if (u < nkb) {
+      ra1[u] = load_frag_e4m3(a1 + u * BLK, g);
+      ra3[u] = load_frag_e4m3(a3 + u * BLK, g);
+      rb[u] = load_frag_e4m3(bq + u * BLK, g);
+      rx[u] = bs[u];
+    }
+  }
+  v4f acc1 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
+  for (int kb0 = 0; kb0 < nkb; kb0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int kb = kb0 + u;
+      if (kb < nkb) {
+        const Frag A1 = decode_e4m3(ra1[u]);
+        const Frag A3 = decode_e4m3(ra3[u]);
+        const Frag B = decode_e4m3(rb[u]);
+        const float f1 = s1[kb] * rx[u], f3 = s3[kb] * rx[u];
+        const int kn = kb + P;
+        if (kn < nkb) {
+          ra1[u] = load_frag_e4m3(a1 + kn * BLK, g);
+          ra3[u] = load_frag_e4m3(a3 + kn * BLK, g);
+          rb[u] = load_frag_e4m3(bq + kn * BLK, g);
+          rx[u] = bs[kn];
+        }
+        const v4f p1 = block_dot(A1, B);
+        const v4f p3 = block_dot(A3, B);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc1[j] = fmaf(p1[j], f1, acc1[j]);
+          acc3[j] = fmaf(p3[j], f3, acc3[j]);
+        }
+      }
+    }
+  }
+
+  __shared__ float red[8][16];
+  float hv[4];
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float gv = round_bf16(acc1[j]);
+    const float uv = round_bf16(acc3[j]);
+    const float h = round_bf16(gv / (1.f + expf(-gv)) * uv);
+    hv[j] = h;
+    amax = fmaxf(amax, fabsf(h));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 16));
+  amax = fmaxf(amax, __shfl_xor(amax, 32));
+  if (g == 0) red[wave][r] = amax;
+  __syncthreads();
+  if (r < nrows) {
+    float m = 0.f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) m = fmaxf(m, red[w][r]);
+    const float sc = m == 0.f ? 1.f : m / E4M3_MAX;
+    const size_t row = (size_t)(row0 + r);
+    *(uint32_t*)(a.hq + row * a.I + ib * BLK + 16 * wave + 4 * g) =
+        pack4_e4m3(hv[0] / sc, hv[1] / sc, hv[2] / sc, hv[3] / sc);
+    if (wave == 0 && g == 0) a.hs[row * nib + ib] = sc;
+  }
+}
+
+template <int P>
+__global__ __launch_bounds__(512) void ffn_down_stream_kernel(FfnArgs a) {
+  const int nob = a.d / BLK, nkb = a.I / BLK;
+  const int tile = blockIdx.x / nob, ob = blockIdx.x - tile * nob;
+  if (tile >= *a.n_tiles) return;
+  const int4 td = a.tiles[tile];
+  const int e = td.x, row0 = td.y, nrows = td.z;
+  const bool sh = e >= a.E;
+  const ExpertPtrs& Pp = sh ? a.shared : a.routed;
+  const size_t eo = sh ? 0 : (size_t)e;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int o = ob * BLK + 16 * wave + r;
+  const uint8_t* aw = Pp.w2 + (eo * a.d + o) * (size_t)a.I;
+  const float* s2 = Pp.s2 + (eo * nob + ob) * nkb;
+  const size_t brow = (size_t)(row0 + min(r, nrows - 1));
+  const uint8_t* bq = a.hq + brow * a.I;
+  const float* bs = a.hs + brow * nkb;
+
+  v8i ra[P], rb[P];
+  float rx[P];
+#pragma unroll
+  for (int u = 0; u < P; ++u) {
+    if (u < nkb) {
+      ra[u] = load_frag_e4m3(aw + u * BLK, g);
+      rb[u] = load_frag_e4m3(bq + u * BLK, g);
+      rx[u] = bs[u];
+    }
+  }
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  for (int kb0 = 0; kb0 < nkb; kb0 += P) {
+#pragma unroll
+    for (int u = 0; u < P; ++u) {
+      const int kb = kb0 + u;
+      if (kb < nkb) {
+        const Frag A = decode_e4m3(ra[u]);
+        const Frag B = decode_e4m3(rb[u]);
+        const float f = s2[kb] * rx[u];
+        const int kn = kb + P;
+        if (kn < nkb) {
+          ra[u] = load_frag_e4m3(aw + kn * BLK, g);
+          rb[u] = load_frag_e4m3(bq + kn * BLK, g);
+          rx[u] = bs[kn];
+        }
+        const v4f p = block_dot(A, B);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = fmaf(p[j], f, acc[j]);
+      }
+    }
+  }
+  if (r < nrows) {
+    const size_t row = (size_t)(row0 + r);
+    uint2 v;
+    v.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+    v.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+    *(uint2*)(a.out + row * a.d + ob * BLK + 16 * wave + 4 * g) = v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-tiled variants for large batches.  A workgroup (8 waves) owns one tile
+// of up to 128 rows and 256 weight rows in two groups of 128:
+//   up-projection:   group 0 = w1 rows of one 128-wide h block, group 1 = the
+//                    w3 rows of the same block (so g and u of an h column meet
+//                    in the same lane and the epilogue fuses SwiGLU + h quant);
+//   down-projection: two consecutive 128-feature blocks of w2.
+// Per 128-deep K block, the e4m3 weight (256 x 128 B) and activation
+// (128 x 128 B) tiles are staged in LDS with 144-byte rows (the 16-byte pad
+// makes the MFMA-layout reads bank-conflict free), double buffered, with the
+// global loads issued two K blocks ahead.  Wave (wr, wc) multiplies rows
+// [64 wr, 64 wr + 64) by weight rows {32 wc .. 32 wc + 31} of both groups:
+// 4 x 4 block products per K block.
+// ---------------------------------------------------------------------------
+
+constexpr int TT_ROWS = 128;             // activation rows per tile
+constexpr int TT_WROWS = 256;            // weight rows per tile
+constexpr int TT_LDS_ROW = 144;          // staged bytes per row
+constexpr int TT_A_BYTES = TT_WROWS * TT_LDS_ROW;
+constexpr int TT_B_BYTES = TT_ROWS * TT_LDS_ROW;
+
+struct TileStage {
+  v4i a[4];  // weight rows tid/8 + 64 i, 16-byte chunk tid%8
+  v4i b[2];  // activation rows tid/8 + 64 j
+};
+
+__device__ __forceinline__ void tile_load(TileStage& st, const uint8_t* const* ap, const uint8_t* const* bp,
+                                          int kb, int chunk) {
+  const int off = kb * BLK + chunk * 16;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) st.a[i] = *(const v4i*)(ap[i] + off);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) st.b[j] = *(const v4i*)(bp[j] + off);
+}
+
+__device__ __forceinline__ void tile_store(const TileStage& st, uint8_t* lds_a, uint8_t* lds_b, int rb, int chunk) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *(v4i*)(lds_a + (rb + 64 * i) * TT_LDS_ROW + chunk * 16) = st.a[i];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) *(v4i*)(lds_b + (rb + 64 * j) * TT_LDS_ROW + chunk * 16) = st.b[j];
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* row, int g) {
+  const v4i lo = *(const v4i*)(row + 16 * g);
+  const v4i hi = *(const v4i*)(row + 64 + 16 * g);
+  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Main loop shared by both projections.  ap: this thread's 4 weight-row
+// pointers (rows tid/8 + 64 i of the tile), bp: its 2 activation-row
+// pointers.  sa[gi][kb]: weight block scale of group gi; bsc[m]: this lane's
+// activation scale row for sub-tile m (indexed by kb).  acc[gi][jt][m].
+__device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const uint8_t* const* ap, const uint8_t* const* bp,
+                                               const float* const* sa, const float* const* bsc, int nkb,
+                                               int mvalid, v4f (&acc)[2][2][4]) {
+  const int tid = threadIdx.x, chunk = tid & 7, rb = tid >> 3;
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int wr = wave >> 2, wc = wave & 3;
+  uint8_t* lds_a[2] = {smem, smem + TT_A_BYTES};
+  uint8_t* lds_b[2] = {smem + 2 * TT_A_BYTES, smem + 2 * TT_A_BYTES + TT_B_BYTES};
+
+  TileStage s0, s1;
+  tile_load(s0, ap, bp, 0, chunk);
+  if (nkb > 1) tile_load(s1, ap, bp, 1, chunk);
+  tile_store(s0, lds_a[0], lds_b[0], rb, chunk);
+  __syncthreads();
+
+  for (int kb0 = 0; kb0 < nkb; kb0 += 2) {
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int kb = kb0 + u;
+      if (kb < nkb) {
+        TileStage& mine = u == 0 ? s0 : s1;   // held stage kb, already in LDS
+        TileStage& next = u == 0 ? s1 : s0;   // holds stage kb + 1
+        if (kb + 2 < nkb) tile_load(mine, ap, bp, kb + 2, chunk);
+        const uint8_t* la = lds_a[u];
+        const uint8_t* lb = lds_b[u];
+        float sb[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) sb[m] = bsc[m][kb];
+        const float s_a0 = sa[0][kb], s_a1 = sa[1][kb];
+        Frag B[4];
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+          if (m < mvalid) B[m] = decode_e4m3(lds_frag(lb + (wr * 64 + 16 * m + r) * TT_LDS_ROW, g));
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const Frag A = decode_e4m3(lds_frag(la + (gi * 128 + wc * 32 + jt * 16 + r) * TT_LDS_ROW, g));
+            const float sg = gi == 0 ? s_a0 : s_a1;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              if (m < mvalid) {
+                const v4f p = block_dot(A, B[m]);
+                const float f = sg * sb[m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[j], f, acc[gi][jt][m][j]);
+              }
+            }
+          }
+        }
+        if (kb + 1 < nkb) tile_store(next, lds_a[u ^ 1], lds_b[u ^ 1], rb, chunk);
+        __syncthreads();
+      }
+    }
+  }
+}
+
+// grid = max_tiles * (I/128), block = 512
+__global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (TT_A_BYTES + TT_B_BYTES)];
   const int nib = a.I / BLK, nkb = a.d / BLK;
   const int tile = blockIdx.x / nib, ib = blockIdx.x - tile * nib;
   if (tile >= *a.n_tiles) return;  // uniform for the whole block, before any barrier
@@ -85,147 +349,158 @@ __global__ __launch_bounds__(512) void ffn_up_kernel(FfnArgs a) {
   const bool sh = e >= a.E;
   const ExpertPtrs& P = sh ? a.shared : a.routed;
   const size_t eo = sh ? 0 : (size_t)e;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int o = ib * BLK + 16 * wave + r;  // w1 / w3 row (h column) this lane loads
-  const uint8_t* a1 = P.w1 + (eo * a.I + o) * (size_t)a.d;
-  const uint8_t* a3 = P.w3 + (eo * a.I + o) * (size_t)a.d;
-  const float* s1 = P.s1 + (eo * nib + ib) * nkb;
-  const float* s3 = P.s3 + (eo * nib + ib) * nkb;
-  const int mvalid = (nrows + 15) >> 4;
+  const int tid = threadIdx.x, rb = tid >> 3;
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int wr = wave >> 2, wc = wave & 3;
 
-  const uint8_t* bq[MT];
-  const float* bs[MT];
+  const uint8_t* ap[4];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const int row = row0 + min(16 * m + r, nrows - 1);
-    const int tok = clampi(a.row_token[row], 0, a.T - 1);
-    bq[m] = a.xq + (size_t)tok * a.d;
-    bs[m] = a.xs + (size_t)tok * nkb;
+  for (int i = 0; i < 4; ++i) {
+    const int row = rb + 64 * i;  // 0..255: w1 rows, then w3 rows of block ib
+    const uint8_t* base = row < 128 ? P.w1 : P.w3;
+    ap[i] = base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d;
   }
-  v4f acc1[MT], acc3[MT];
+  const uint8_t* bp[2];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    acc1[m] = v4f{0.f, 0.f, 0.f, 0.f};
-    acc3[m] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < 2; ++j) {
+    const int tok = clampi(a.row_token[row0 + min(rb + 64 * j, nrows - 1)], 0, a.T - 1);
+    bp[j] = a.xq + (size_t)tok * a.d;
   }
-  for (int kb = 0; kb < nkb; ++kb) {
-    const Frag A1 = decode_e4m3(load_frag_e4m3(a1 + kb * BLK, g));
-    const Frag A3 = decode_e4m3(load_frag_e4m3(a3 + kb * BLK, g));
-    const float sw1 = s1[kb], sw3 = s3[kb];
+  const float* sa[2] = {P.s1 + (eo * nib + ib) * nkb, P.s3 + (eo * nib + ib) * nkb};
+  const float* bsc[4];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < mvalid) {
-        const Frag B = decode_e4m3(load_frag_e4m3(bq[m] + kb * BLK, g));
-        const float sx = bs[m][kb];
-        const v4f p1 = block_dot(A1, B);
-        const v4f p3 = block_dot(A3, B);
-        const float f1 = sw1 * sx, f3 = sw3 * sx;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc1[m][j] = fmaf(p1[j], f1, acc1[m][j]);
-          acc3[m][j] = fmaf(p3[j], f3, acc3[m][j]);
-        }
-      }
-    }
+  for (int m = 0; m < 4; ++m) {
+    const int tok = clampi(a.row_token[row0 + min(wr * 64 + 16 * m + r, nrows - 1)], 0, a.T - 1);
+    bsc[m] = a.xs + (size_t)tok * nkb;
   }
+  const int mvalid = min(4, max(0, (nrows - wr * 64 + 15) >> 4));
+  v4f acc[2][2][4];
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
+  tiled_mainloop(smem, ap, bp, sa, bsc, nkb, mvalid, acc);
 
-  // epilogue: h = bf16(silu(bf16 g) * bf16 u); per-row amax over the 128 columns
-  __shared__ float red[8][MT * 16];
-  float hv[MT][4];
+  // epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32 columns x 64
+  // rows; per-row amax over the block's 128 columns (4 waves) via LDS
+  float* red = (float*)smem;  // [2][4][64], staging buffers are no longer read
+  float hv[2][4][4];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
+  for (int m = 0; m < 4; ++m) {
     float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float gv = round_bf16(acc1[m][j]);
-      const float uv = round_bf16(acc3[m][j]);
-      const float h = round_bf16(gv / (1.f + expf(-gv)) * uv);
-      hv[m][j] = h;
-      amax = fmaxf(amax, fabsf(h));
-    }
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float gv = round_bf16(acc[0][jt][m][j]);
+        const float uv = round_bf16(acc[1][jt][m][j]);
+        const float h = round_bf16(gv / (1.f + expf(-gv)) * uv);
+        hv[jt][m][j] = h;
+        amax = fmaxf(amax, fabsf(h));
+      }
     amax = fmaxf(amax, __shfl_xor(amax, 16));
     amax = fmaxf(amax, __shfl_xor(amax, 32));
-    if (g == 0) red[wave][m * 16 + r] = amax;
+    if (g == 0) red[(wr * 4 + wc) * 64 + 16 * m + r] = amax;
   }
   __syncthreads();
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (m < mvalid && 16 * m + r < nrows) {
+  for (int m = 0; m < 4; ++m) {
+    const int rr = wr * 64 + 16 * m + r;
+    if (rr < nrows) {
       float amax = 0.f;
 #pragma unroll
-      for (int w = 0; w < 8; ++w) amax = fmaxf(amax, red[w][m * 16 + r]);
+      for (int c = 0; c < 4; ++c) amax = fmaxf(amax, red[(wr * 4 + c) * 64 + 16 * m + r]);
       const float sc = amax == 0.f ? 1.f : amax / E4M3_MAX;
-      const size_t row = (size_t)(row0 + 16 * m + r);
-      const uint32_t q = pack4_e4m3(hv[m][0] / sc, hv[m][1] / sc, hv[m][2] / sc, hv[m][3] / sc);
-      *(uint32_t*)(a.hq + row * a.I + ib * BLK + 16 * wave + 4 * g) = q;
-      if (wave == 0 && g == 0) a.hs[row * nib + ib] = sc;
+      const size_t row = (size_t)(row0 + rr);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+        *(uint32_t*)(a.hq + row * a.I + ib * BLK + wc * 32 + jt * 16 + 4 * g) =
+            pack4_e4m3(hv[jt][m][0] / sc, hv[jt][m][1] / sc, hv[jt][m][2] / sc, hv[jt][m][3] / sc);
+      if (wc == 0 && g == 0) a.hs[row * nib + ib] = sc;
     }
   }
 }
 
-// grid = max_tiles * (d/128), block = 512 (8 waves)
-template <int MT>
-__global__ __launch_bounds__(512) void ffn_down_kernel(FfnArgs a) {
+// grid = max_tiles * ceil(d/256), block = 512
+__global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (TT_A_BYTES + TT_B_BYTES)];
   const int nob = a.d / BLK, nkb = a.I / BLK;
-  const int tile = blockIdx.x / nob, ob = blockIdx.x - tile * nob;
+  const int nob2 = (nob + 1) >> 1;
+  const int tile = blockIdx.x / nob2, ob = blockIdx.x - tile * nob2;
   if (tile >= *a.n_tiles) return;
   const int4 td = a.tiles[tile];
   const int e = td.x, row0 = td.y, nrows = td.z;
   const bool sh = e >= a.E;
   const ExpertPtrs& P = sh ? a.shared : a.routed;
   const size_t eo = sh ? 0 : (size_t)e;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int o = ob * BLK + 16 * wave + r;
-  const uint8_t* aw = P.w2 + (eo * a.d + o) * (size_t)a.I;
-  const float* s2 = P.s2 + (eo * nob + ob) * nkb;
-  const int mvalid = (nrows + 15) >> 4;
+  const int tid = threadIdx.x, rb = tid >> 3;
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int wr = wave >> 2, wc = wave & 3;
 
-  const uint8_t* bq[MT];
-  const float* bs[MT];
+  const uint8_t* ap[4];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    const size_t row = (size_t)(row0 + min(16 * m + r, nrows - 1));
-    bq[m] = a.hq + row * a.I;
-    bs[m] = a.hs + row * nkb;
+  for (int i = 0; i < 4; ++i) {
+    const int o = min(ob * 256 + rb + 64 * i, a.d - 1);  // a ragged last pair of blocks reads a valid row
+    ap[i] = P.w2 + (eo * a.d + o) * (size_t)a.I;
   }
-  v4f acc[MT];
+  const uint8_t* bp[2];
 #pragma unroll
-  for (int m = 0; m < MT; ++m) acc[m] = v4f{0.f, 0.f, 0.f, 0.f};
-  for (int kb = 0; kb < nkb; ++kb) {
-    const Frag A = decode_e4m3(load_frag_e4m3(aw + kb * BLK, g));
-    const float sw = s2[kb];
+  for (int j = 0; j < 2; ++j) bp[j] = a.hq + (size_t)(row0 + min(rb + 64 * j, nrows - 1)) * a.I;
+  const float* sa[2] = {P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb,
+                        P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb};
+  const float* bsc[4];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      if (m < mvalid) {
-        const Frag B = decode_e4m3(load_frag_e4m3(bq[m] + kb * BLK, g));
-        const float f = sw * bs[m][kb];
-        const v4f p = block_dot(A, B);
+  for (int m = 0; m < 4; ++m) bsc[m] = a.hs + (size_t)(row0 + min(wr * 64 + 16 * m + r, nrows - 1)) * nkb;
+  const int mvalid = min(4, max(0, (nrows - wr * 64 + 15) >> 4));
+  v4f acc[2][2][4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[m][j] = fmaf(p[j], f, acc[m][j]);
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
+  tiled_mainloop(smem, ap, bp, sa, bsc, nkb, mvalid, acc);
+
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int rr = wr * 64 + 16 * m + r;
+    if (rr < nrows) {
+      const size_t row = (size_t)(row0 + rr);
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        if (2 * ob + gi < nob) {
+#pragma unroll
+          for (int jt = 0; jt < 2; ++jt) {
+            const v4f v = acc[gi][jt][m];
+            uint2 o;
+            o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+            o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+            *(uint2*)(a.out + row * a.d + (2 * ob + gi) * BLK + wc * 32 + jt * 16 + 4 * g) = o;
+          }
+        }
       }
-    }
-  }
-#pragma unroll
-  for (int m = 0; m < MT; ++m) {
-    if (m < mvalid && 16 * m + r < nrows) {
-      const size_t row = (size_t)(row0 + 16 * m + r);
-      uint2 v;
-      v.x = (uint32_t)f32_to_bf16(acc[m][0]) | ((uint32_t)f32_to_bf16(acc[m][1]) << 16);
-      v.y = (uint32_t)f32_to_bf16(acc[m][2]) | ((uint32_t)f32_to_bf16(acc[m][3]) << 16);
-      *(uint2*)(a.out + row * a.d + ob * BLK + 16 * wave + 4 * g) = v;
     }
   }
 }
 
-template <int MT>
-hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
-  const int64_t g1 = max_tiles * (a.I / BLK), g2 = max_tiles * (a.d / BLK);
+hipError_t launch_gemms(const FfnArgs& a, int tile_rows, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
+  const bool stream = tile_rows == 16;
+  const int64_t g1 = max_tiles * (a.I / BLK);
+  const int64_t g2 = max_tiles * (stream ? a.d / BLK : (a.d / BLK + 1) / 2);
   if (ev) (void)hipEventRecord(ev[0], s);
-  hipLaunchKernelGGL(ffn_up_kernel<MT>, dim3((unsigned)g1), dim3(512), 0, s, a);
+  if (stream)
+    hipLaunchKernelGGL(ffn_up_stream_kernel<STREAM_DEPTH>, dim3((unsigned)g1), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(ffn_up_tiled_kernel, dim3((unsigned)g1), dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev) (void)hipEventRecord(ev[1], s);
-  hipLaunchKernelGGL(ffn_down_kernel<MT>, dim3((unsigned)g2), dim3(512), 0, s, a);
+  if (stream)
+    hipLaunchKernelGGL(ffn_down_stream_kernel<STREAM_DEPTH>, dim3((unsigned)g2), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(ffn_down_tiled_kernel, dim3((unsigned)g2), dim3(512), 0, s, a);
   err = hipGetLastError();
   if (ev) (void)hipEventRecord(ev[2], s);
   return err;
@@ -234,9 +509,9 @@ hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipE
 }  // namespace
 
 int ffn_tile_rows(int64_t T) {
-  if (T <= 16) return 16;
-  if (T <= 32) return 32;
-  if (T <= 64) return 64;
+  // small batches: 16-row tiles on the streaming kernels (experts then hold a
+  // few rows each and the weights dominate the traffic)
+  if (T <= STREAM_MAX_TOKENS) return 16;
   return 128;
 }
 
@@ -271,12 +546,7 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
   a.hq = hq;
   a.hs = hs;
   a.out = out;
-  switch (NT) {
-    case 16: return launch_gemms<1>(a, max_tiles, s, ev);
-    case 32: return launch_gemms<2>(a, max_tiles, s, ev);
-    case 64: return launch_gemms<4>(a, max_tiles, s, ev);
-    default: return launch_gemms<8>(a, max_tiles, s, ev);
-  }
+  return launch_gemms(a, NT, max_tiles, s, ev);
 }
 
 }  // namespace moe

@@ -107,15 +107,35 @@ __global__ __launch_bounds__(256) void gate_select_kernel(const float* __restric
   const int tt = live ? t : T - 1;
   const int epg = E / G;
 
+  // logits: the K-split partial sums, added in split order; eight splits of
+  // all four experts are loaded before they are added
+  float z[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* zp = zpart + (size_t)tt * E + lane;
+  const size_t split_stride = (size_t)T * E;
+  int ks = 0;
+  for (; ks + 8 <= ksplit; ks += 8) {
+    float v[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[j][i] = (lane + 64 * i < E) ? zp[(ks + j) * split_stride + 64 * i] : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] += v[j][i];
+  }
+  for (; ks < ksplit; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) z[i] += zp[ks * split_stride + 64 * i];
+
   float b[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
     b[i] = -INFINITY;
     if (e < E) {
-      float z = 0.f;
-      for (int ks = 0; ks < ksplit; ++ks) z += zpart[((size_t)ks * T + tt) * E + e];
-      const float s = 1.f / (1.f + expf(-z));
+      const float s = 1.f / (1.f + expf(-z[i]));
       float v = s + bias[e];
       if (v != v) v = -INFINITY;  // NaN never wins a comparison below
       s_score[wave][e] = s;
