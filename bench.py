@@ -162,6 +162,8 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skewed", "stack4"])
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
@@ -176,6 +178,16 @@ def main():
 
     dev = "cuda:0"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 3}))
+        return
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
     data = synth.make_workload(args.workload, device=dev)

@@ -20,7 +20,8 @@
  *  - bf16 tensors are passed as uint16_t (the bit pattern).  FP8 tensors are
  *    OCP e4m3fn codes (uint8_t), with one float32 scale per 128x128 block.
  *  - Row-major layouts throughout.  d_model and inter must be multiples of
- *    128; n_experts <= 256; experts per group >= 2; topk <= 32.
+ *    128 and at most 16384; n_experts <= 256 and a multiple of 16; experts
+ *    per group >= 2; n_groups <= 64; topk <= 32.
  *  - Errors: arguments are checked on the host before anything is enqueued;
  *    a negative moe_status is returned and nothing runs.  A failed launch
  *    returns MOE_ERR_HIP.  tokens == 0 is a valid no-op.
@@ -166,7 +167,9 @@ int moe_forward_timed(const moe_dims* dims, const moe_weights* weights, int64_t 
 
 /* Fused residual add + RMSNorm ("MoE update", rmsnorm excerpt, residual branch):
  *   r = float(x) + float(residual);  residual <- bf16(r);
- *   out = bf16(gain * r * rsqrt(mean(r^2) + eps))   (fp32 arithmetic)
+ *   out = bf16(gain * r * rsqrt(mean(r^2) + eps))
+ * The normalisation is evaluated in fp64 and rounded once to bf16, so the
+ * result does not depend on the reduction order.
  *   x, residual, out  bf16 [T][d] (16-byte aligned; out may alias x); gain fp32 [d].
  * d must be a multiple of 128 and at most 16384.  No workspace. */
 int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* residual,

@@ -61,7 +61,7 @@ int check_dims(const moe_dims* p) {
   if (d.topk > d.topk_groups * (d.n_experts / d.n_groups)) return MOE_ERR_INVALID_ARG;
   if (!isfinite(d.route_scale)) return MOE_ERR_INVALID_ARG;
   if (d.d_model % BLK != 0 || d.inter % BLK != 0) return MOE_ERR_UNSUPPORTED;
-  if (d.d_model > 65536 || d.inter > 65536) return MOE_ERR_UNSUPPORTED;
+  if (d.d_model > 16384 || d.inter > 16384) return MOE_ERR_UNSUPPORTED;  // at most 128 K blocks per projection
   if (d.n_experts > 256 || d.n_experts % 16 != 0) return MOE_ERR_UNSUPPORTED;
   if (d.n_groups > 64 || d.n_experts / d.n_groups < 2) return MOE_ERR_UNSUPPORTED;
   if (d.topk > 32) return MOE_ERR_UNSUPPORTED;

@@ -244,103 +244,192 @@ __global__ __launch_bounds__(512) void ffn_down_stream_kernel(FfnArgs a) {
 // 4 x 4 block products per K block.
 // ---------------------------------------------------------------------------
 
-constexpr int TT_ROWS = 128;             // activation rows per tile
-constexpr int TT_WROWS = 256;            // weight rows per tile
-constexpr int TT_LDS_ROW = 144;          // staged bytes per row
-constexpr int TT_A_BYTES = TT_WROWS * TT_LDS_ROW;
-constexpr int TT_B_BYTES = TT_ROWS * TT_LDS_ROW;
+constexpr int TT_ROWS = 128;                 // activation rows per tile
+constexpr int TT_WROWS = 256;                // weight rows per tile
+constexpr int TT_A_BYTES = TT_WROWS * BLK;   // one K block of the weight tile
+constexpr int TT_B_BYTES = TT_ROWS * BLK;    // one K block of the activation tile
+constexpr int TT_S_BYTES = TT_ROWS * 4;      // activation scales of one K block
+constexpr int TT_STAGE = TT_A_BYTES + TT_B_BYTES + TT_S_BYTES;
+constexpr int TT_NSTAGE = 3;
+constexpr int TT_SMEM = TT_NSTAGE * TT_STAGE;
+constexpr int TT_MAX_KB = 128;               // K blocks per projection the tiled kernels support
 
-struct TileStage {
-  v4i a[4];  // weight rows tid/8 + 64 i, 16-byte chunk tid%8
-  v4i b[2];  // activation rows tid/8 + 64 j
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// LDS holds each 128-byte row unpadded with its 16-byte chunks permuted:
+// chunk c of row r sits at slot c ^ swz(r).  Sixteen consecutive rows then
+// spread one MFMA-layout read (same chunk, rows r0..r0+15) over all banks.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Global -> LDS copies (global_load_lds) of one K block.  Wave w copies
+// weight rows [32w, 32w + 32) (four 8-row pieces), activation rows
+// [16w, 16w + 16) (two pieces) and, for w < 2, the scales of activation rows
+// [64w, 64w + 64).  Lane l of a piece covers row piece_row0 + l/8 and LDS slot
+// l%8, so it fetches global chunk (l%8) ^ swz(row).
+struct TileSrc {
+  const uint8_t* a[4];  // this lane's source rows for the four weight pieces (chunk applied)
+  const uint8_t* b[2];  // ... for the two activation pieces
+  const float* s;       // scale row of activation row 64w + lane (waves 0, 1)
 };
 
-__device__ __forceinline__ void tile_load(TileStage& st, const uint8_t* const* ap, const uint8_t* const* bp,
-                                          int kb, int chunk) {
-  const int off = kb * BLK + chunk * 16;
+__device__ __forceinline__ void tile_issue(const TileSrc& src, uint8_t* stage, int kb, int wave) {
+  const int off = kb * BLK;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) st.a[i] = *(const v4i*)(ap[i] + off);
+  for (int i = 0; i < 4; ++i)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.a[i] + off), (lds_ptr_t)(stage + (wave * 4 + i) * 1024), 16, 0, 0);
 #pragma unroll
-  for (int j = 0; j < 2; ++j) st.b[j] = *(const v4i*)(bp[j] + off);
+  for (int j = 0; j < 2; ++j)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[j] + off),
+                                     (lds_ptr_t)(stage + TT_A_BYTES + (wave * 2 + j) * 1024), 16, 0, 0);
+  if (wave < 2)
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.s + kb), (lds_ptr_t)(stage + TT_A_BYTES + TT_B_BYTES + wave * 256),
+                                     4, 0, 0);
 }
 
-__device__ __forceinline__ void tile_store(const TileStage& st, uint8_t* lds_a, uint8_t* lds_b, int rb, int chunk) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) *(v4i*)(lds_a + (rb + 64 * i) * TT_LDS_ROW + chunk * 16) = st.a[i];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) *(v4i*)(lds_b + (rb + 64 * j) * TT_LDS_ROW + chunk * 16) = st.b[j];
+// wait until this wave's copies of every stage but the newest one have landed
+__device__ __forceinline__ void tile_wait_all_but_newest(int wave, bool newest_issued) {
+  if (!newest_issued) {
+    wait_vmcnt<0>();
+  } else if (wave < 2) {
+    wait_vmcnt<7>();
+  } else {
+    wait_vmcnt<6>();
+  }
 }
 
-__device__ __forceinline__ v8i lds_frag(const uint8_t* row, int g) {
-  const v4i lo = *(const v4i*)(row + 16 * g);
-  const v4i hi = *(const v4i*)(row + 64 + 16 * g);
+// Workgroup barrier of the copy pipeline.  Each wave has already waited
+// (wait_vmcnt) for its own global->LDS copies of the stage the barrier
+// publishes, and the pipeline writes LDS in no other way, so no memory fence
+// is needed: the fence __syncthreads adds would also wait for the copies of
+// the stage after it.  The empty asm statements keep the compiler from moving
+// LDS accesses across the barrier.
+__device__ __forceinline__ void pipeline_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
+  const uint8_t* row = base + r * BLK;
+  const int z = swz(r);
+  const v4i lo = *(const v4i*)(row + 16 * (g ^ z));
+  const v4i hi = *(const v4i*)(row + 16 * ((4 + g) ^ z));
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
-// Main loop shared by both projections.  ap: this thread's 4 weight-row
-// pointers (rows tid/8 + 64 i of the tile), bp: its 2 activation-row
-// pointers.  sa[gi][kb]: weight block scale of group gi; bsc[m]: this lane's
-// activation scale row for sub-tile m (indexed by kb).  acc[gi][jt][m].
-__device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const uint8_t* const* ap, const uint8_t* const* bp,
-                                               const float* const* sa, const float* const* bsc, int nkb,
-                                               int mvalid, v4f (&acc)[2][2][4]) {
-  const int tid = threadIdx.x, chunk = tid & 7, rb = tid >> 3;
-  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+// Main loop shared by both projections.  src: this lane's DMA sources.
+// sa[gi][kb]: weight block scale of group gi.  acc[gi][jt][m].  mvalid
+// (wave-uniform): 16-row sub-tiles of this wave that hold rows.
+template <bool FULL>
+__device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const TileSrc& src, const float* const* sa,
+                                               int nkb, int mvalid, v4f (&acc)[2][2][4]) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
-  uint8_t* lds_a[2] = {smem, smem + TT_A_BYTES};
-  uint8_t* lds_b[2] = {smem + 2 * TT_A_BYTES, smem + 2 * TT_A_BYTES + TT_B_BYTES};
 
-  TileStage s0, s1;
-  tile_load(s0, ap, bp, 0, chunk);
-  if (nkb > 1) tile_load(s1, ap, bp, 1, chunk);
-  tile_store(s0, lds_a[0], lds_b[0], rb, chunk);
+  // the weight block scales of the whole K range, read once (published by the first barrier)
+  for (int i = threadIdx.x; i < 2 * TT_MAX_KB; i += blockDim.x) {
+    const int gi = i / TT_MAX_KB, kb = i - gi * TT_MAX_KB;
+    if (kb < nkb) lsa[i] = sa[gi][kb];
+  }
+  tile_issue(src, smem, 0, wave);
+  if (nkb > 1) tile_issue(src, smem + TT_STAGE, 1, wave);
+  tile_wait_all_but_newest(wave, nkb > 1);
   __syncthreads();
 
-  for (int kb0 = 0; kb0 < nkb; kb0 += 2) {
+  int cur = 0;  // stage buffer holding K block kb
+  for (int kb = 0; kb < nkb; ++kb) {
+    const bool ahead = kb + 2 < nkb;
+    if (ahead) {
+      const int nb = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
+      tile_issue(src, smem + nb * TT_STAGE, kb + 2, wave);
+    }
+    const uint8_t* la = smem + cur * TT_STAGE;
+    const uint8_t* lb = la + TT_A_BYTES;
+    const float* ls = (const float*)(lb + TT_B_BYTES);
+    const float s_a0 = lsa[kb], s_a1 = lsa[TT_MAX_KB + kb];
+    Frag B[4];
+    float sb[4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int kb = kb0 + u;
-      if (kb < nkb) {
-        TileStage& mine = u == 0 ? s0 : s1;   // held stage kb, already in LDS
-        TileStage& next = u == 0 ? s1 : s0;   // holds stage kb + 1
-        if (kb + 2 < nkb) tile_load(mine, ap, bp, kb + 2, chunk);
-        const uint8_t* la = lds_a[u];
-        const uint8_t* lb = lds_b[u];
-        float sb[4];
+    for (int m = 0; m < 4; ++m) {
+      if (FULL || m < mvalid) {
+        B[m] = decode_e4m3(lds_frag(lb, wr * 64 + 16 * m + r, g));
+        sb[m] = ls[wr * 64 + 16 * m + r];
+      }
+    }
 #pragma unroll
-        for (int m = 0; m < 4; ++m) sb[m] = bsc[m][kb];
-        const float s_a0 = sa[0][kb], s_a1 = sa[1][kb];
-        Frag B[4];
+    for (int gi = 0; gi < 2; ++gi) {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
-          if (m < mvalid) B[m] = decode_e4m3(lds_frag(lb + (wr * 64 + 16 * m + r) * TT_LDS_ROW, g));
+      for (int jt = 0; jt < 2; ++jt) {
+        const Frag A = decode_e4m3(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
+        const float sg = gi == 0 ? s_a0 : s_a1;
+        if constexpr (FULL) {
+          // four independent accumulation chains, issued round-robin
+          v4f p[4];
 #pragma unroll
-        for (int gi = 0; gi < 2; ++gi) {
+          for (int m = 0; m < 4; ++m) p[m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            const Frag A = decode_e4m3(lds_frag(la + (gi * 128 + wc * 32 + jt * 16 + r) * TT_LDS_ROW, g));
-            const float sg = gi == 0 ? s_a0 : s_a1;
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              if (m < mvalid) {
-                const v4f p = block_dot(A, B[m]);
-                const float f = sg * sb[m];
+            for (int m = 0; m < 4; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], p[m], 0, 0, 0);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[j], f, acc[gi][jt][m][j]);
-              }
+          for (int m = 0; m < 4; ++m) {
+            const float f = sg * sb[m];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[m][j], f, acc[gi][jt][m][j]);
+          }
+        } else {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            if (m < mvalid) {
+              const v4f p = block_dot(A, B[m]);
+              const float f = sg * sb[m];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[j], f, acc[gi][jt][m][j]);
             }
           }
         }
-        if (kb + 1 < nkb) tile_store(next, lds_a[u ^ 1], lds_b[u ^ 1], rb, chunk);
-        __syncthreads();
       }
     }
+    if (kb + 1 < nkb) tile_wait_all_but_newest(wave, ahead);
+    pipeline_barrier();
+    cur = cur == 2 ? 0 : cur + 1;
   }
+}
+
+// DMA source pointers of this lane.  wrow(i): weight row of tile row i
+// (0..255); arow(j): activation row pointer of tile row j (0..127);
+// srow(j): its scale row.
+template <typename WRow, typename ARow, typename SRow>
+__device__ __forceinline__ TileSrc make_tile_src(WRow wrow, ARow arow, SRow srow) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int slot = lane & 7;
+  TileSrc t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (wave * 4 + i) * 8 + (lane >> 3);
+    t.a[i] = wrow(row) + 16 * (slot ^ swz(row));
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = (wave * 2 + j) * 8 + (lane >> 3);
+    t.b[j] = arow(row) + 16 * (slot ^ swz(row));
+  }
+  t.s = srow(min(wave, 1) * 64 + lane);
+  return t;
 }
 
 // grid = max_tiles * (I/128), block = 512
 __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (TT_A_BYTES + TT_B_BYTES)];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TT_SMEM];
+  __shared__ float lsa[2 * TT_MAX_KB];
   const int nib = a.I / BLK, nkb = a.d / BLK;
   const int tile = blockIdx.x / nib, ib = blockIdx.x - tile * nib;
   if (tile >= *a.n_tiles) return;  // uniform for the whole block, before any barrier
@@ -349,31 +438,26 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
   const bool sh = e >= a.E;
   const ExpertPtrs& P = sh ? a.shared : a.routed;
   const size_t eo = sh ? 0 : (size_t)e;
-  const int tid = threadIdx.x, rb = tid >> 3;
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
 
-  const uint8_t* ap[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = rb + 64 * i;  // 0..255: w1 rows, then w3 rows of block ib
-    const uint8_t* base = row < 128 ? P.w1 : P.w3;
-    ap[i] = base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d;
-  }
-  const uint8_t* bp[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int tok = clampi(a.row_token[row0 + min(rb + 64 * j, nrows - 1)], 0, a.T - 1);
-    bp[j] = a.xq + (size_t)tok * a.d;
-  }
+  const int* rt = a.row_token;
+  const TileSrc src = make_tile_src(
+      [&](int row) {  // 0..127: w1 rows of block ib, 128..255: w3 rows
+        const uint8_t* base = row < 128 ? P.w1 : P.w3;
+        return base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d;
+      },
+      [&](int row) {
+        const int tok = clampi(rt[row0 + min(row, nrows - 1)], 0, a.T - 1);
+        return a.xq + (size_t)tok * a.d;
+      },
+      [&](int row) {
+        const int tok = clampi(rt[row0 + min(row, nrows - 1)], 0, a.T - 1);
+        return a.xs + (size_t)tok * nkb;
+      });
   const float* sa[2] = {P.s1 + (eo * nib + ib) * nkb, P.s3 + (eo * nib + ib) * nkb};
-  const float* bsc[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) {
-    const int tok = clampi(a.row_token[row0 + min(wr * 64 + 16 * m + r, nrows - 1)], 0, a.T - 1);
-    bsc[m] = a.xs + (size_t)tok * nkb;
-  }
-  const int mvalid = min(4, max(0, (nrows - wr * 64 + 15) >> 4));
+  const int mvalid = __builtin_amdgcn_readfirstlane(min(4, max(0, (nrows - wr * 64 + 15) >> 4)));
   v4f acc[2][2][4];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi)
@@ -381,7 +465,10 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  tiled_mainloop(smem, ap, bp, sa, bsc, nkb, mvalid, acc);
+  if (mvalid == 4)
+    tiled_mainloop<true>(smem, lsa, src, sa, nkb, mvalid, acc);
+  else
+    tiled_mainloop<false>(smem, lsa, src, sa, nkb, mvalid, acc);
 
   // epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32 columns x 64
   // rows; per-row amax over the block's 128 columns (4 waves) via LDS
@@ -425,7 +512,8 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
 
 // grid = max_tiles * ceil(d/256), block = 512
 __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * (TT_A_BYTES + TT_B_BYTES)];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[TT_SMEM];
+  __shared__ float lsa[2 * TT_MAX_KB];
   const int nob = a.d / BLK, nkb = a.I / BLK;
   const int nob2 = (nob + 1) >> 1;
   const int tile = blockIdx.x / nob2, ob = blockIdx.x - tile * nob2;
@@ -435,25 +523,20 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
   const bool sh = e >= a.E;
   const ExpertPtrs& P = sh ? a.shared : a.routed;
   const size_t eo = sh ? 0 : (size_t)e;
-  const int tid = threadIdx.x, rb = tid >> 3;
+  const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
 
-  const uint8_t* ap[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int o = min(ob * 256 + rb + 64 * i, a.d - 1);  // a ragged last pair of blocks reads a valid row
-    ap[i] = P.w2 + (eo * a.d + o) * (size_t)a.I;
-  }
-  const uint8_t* bp[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) bp[j] = a.hq + (size_t)(row0 + min(rb + 64 * j, nrows - 1)) * a.I;
+  const TileSrc src = make_tile_src(
+      [&](int row) {  // a ragged last pair of blocks reads a valid row
+        const int o = min(ob * 256 + row, a.d - 1);
+        return P.w2 + (eo * a.d + o) * (size_t)a.I;
+      },
+      [&](int row) { return a.hq + (size_t)(row0 + min(row, nrows - 1)) * a.I; },
+      [&](int row) { return a.hs + (size_t)(row0 + min(row, nrows - 1)) * nkb; });
   const float* sa[2] = {P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb,
                         P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb};
-  const float* bsc[4];
-#pragma unroll
-  for (int m = 0; m < 4; ++m) bsc[m] = a.hs + (size_t)(row0 + min(wr * 64 + 16 * m + r, nrows - 1)) * nkb;
-  const int mvalid = min(4, max(0, (nrows - wr * 64 + 15) >> 4));
+  const int mvalid = __builtin_amdgcn_readfirstlane(min(4, max(0, (nrows - wr * 64 + 15) >> 4)));
   v4f acc[2][2][4];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi)
@@ -461,7 +544,10 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  tiled_mainloop(smem, ap, bp, sa, bsc, nkb, mvalid, acc);
+  if (mvalid == 4)
+    tiled_mainloop<true>(smem, lsa, src, sa, nkb, mvalid, acc);
+  else
+    tiled_mainloop<false>(smem, lsa, src, sa, nkb, mvalid, acc);
 
 #pragma unroll
   for (int m = 0; m < 4; ++m) {

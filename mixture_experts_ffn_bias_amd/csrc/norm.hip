@@ -1,14 +1,34 @@
 // Fused residual add + RMSNorm ("DeepSeek-V3.2-Exp · MoE update", rmsnorm
 // excerpt, residual branch): r = float(x) + float(residual); the residual
-// becomes bf16(r); the output is bf16(gain * (r * rsqrt(mean(r^2) + eps))),
-// all arithmetic in fp32.  One workgroup per token; each thread keeps its
-// share of r in registers, so `out` may alias `x`.
+// becomes bf16(r); the output is bf16(gain * r * rsqrt(mean(r^2) + eps)).
+// The pages evaluate the normalisation in fp32 with an unspecified reduction
+// order; here it is evaluated exactly enough to be order-independent: the
+// sum of squares, the scale and the products in fp64, then one correct
+// rounding to bf16.  (The e4m3 quantisation of the normalised rows downstream
+// turns a one-ulp difference of a block maximum into a rescaled block, so the
+// normalised values are worth getting exactly right.)  The residual add is
+// the pages' fp32 add (exact for two bf16 values).  One workgroup per token;
+// each thread keeps its share of r in registers, so `out` may alias `x`.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
+
+// bf16 nearest (ties to even) of a double, rounded once: the conversion to
+// float rounds to odd (inexact results get their last bit set), which keeps
+// the following round-to-nearest-even to bf16 correct.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  float f = (float)v;
+  const double back = (double)f;
+  if (back != v) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 1u) == 0u) u += ((back < v) == (f >= 0.f)) ? 1u : 0xFFFFFFFFu;
+    f = __uint_as_float(u);
+  }
+  return f32_to_bf16(f);
+}
 
 constexpr int NORM_THREADS = 256;
 constexpr int NORM_CHUNKS = 8;  // 8-element chunks per thread: d <= 256 * 8 * 8 = 16384
@@ -17,35 +37,36 @@ __global__ __launch_bounds__(NORM_THREADS) void add_rmsnorm_kernel(const uint16_
                                                                     uint16_t* __restrict__ res,
                                                                     const float* __restrict__ gain, float eps,
                                                                     int d, uint16_t* out) {
-  __shared__ float s_part[NORM_THREADS / 64];
+  __shared__ double s_part[NORM_THREADS / 64];
   const size_t t = blockIdx.x;
   const int nch = d / 8;
-  float r[NORM_CHUNKS][8];
-  float ss = 0.f;
+  uint32_t xw[NORM_CHUNKS][4], rw[NORM_CHUNKS][4];  // the raw bf16 pairs of x and the residual
+  double ss = 0.0;
 #pragma unroll
   for (int i = 0; i < NORM_CHUNKS; ++i) {
     const int c = threadIdx.x + NORM_THREADS * i;
     if (c < nch) {
       const uint4 xv = *(const uint4*)(x + t * d + c * 8);
       const uint4 rv = *(const uint4*)(res + t * d + c * 8);
-      const uint32_t xu[4] = {xv.x, xv.y, xv.z, xv.w};
-      const uint32_t ru[4] = {rv.x, rv.y, rv.z, rv.w};
+      xw[i][0] = xv.x; xw[i][1] = xv.y; xw[i][2] = xv.z; xw[i][3] = xv.w;
+      rw[i][0] = rv.x; rw[i][1] = rv.y; rw[i][2] = rv.z; rw[i][3] = rv.w;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        r[i][2 * j] = bf16_to_f32(xu[j] & 0xFFFFu) + bf16_to_f32(ru[j] & 0xFFFFu);
-        r[i][2 * j + 1] = bf16_to_f32(xu[j] >> 16) + bf16_to_f32(ru[j] >> 16);
+        // the sum of two bf16 values is exact in fp64
+        const double lo = (double)bf16_to_f32(xw[i][j] & 0xFFFFu) + (double)bf16_to_f32(rw[i][j] & 0xFFFFu);
+        const double hi = (double)bf16_to_f32(xw[i][j] >> 16) + (double)bf16_to_f32(rw[i][j] >> 16);
+        ss = fma(lo, lo, ss);
+        ss = fma(hi, hi, ss);
       }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) ss = fmaf(r[i][j], r[i][j], ss);
     }
   }
   for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
   if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
   __syncthreads();
-  float tot = 0.f;
+  double tot = 0.0;
 #pragma unroll
   for (int i = 0; i < NORM_THREADS / 64; ++i) tot += s_part[i];
-  const float rs = 1.f / sqrtf(tot / (float)d + eps);
+  const double rs = 1.0 / sqrt(tot / (double)d + (double)eps);
 #pragma unroll
   for (int i = 0; i < NORM_CHUNKS; ++i) {
     const int c = threadIdx.x + NORM_THREADS * i;
@@ -56,9 +77,13 @@ __global__ __launch_bounds__(NORM_THREADS) void add_rmsnorm_kernel(const uint16_
       uint32_t ro[4], oo[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        ro[j] = (uint32_t)f32_to_bf16(r[i][2 * j]) | ((uint32_t)f32_to_bf16(r[i][2 * j + 1]) << 16);
-        oo[j] = (uint32_t)f32_to_bf16(gg[2 * j] * (r[i][2 * j] * rs)) |
-                ((uint32_t)f32_to_bf16(gg[2 * j + 1] * (r[i][2 * j + 1] * rs)) << 16);
+        const float xl = bf16_to_f32(xw[i][j] & 0xFFFFu), xh = bf16_to_f32(xw[i][j] >> 16);
+        const float rl = bf16_to_f32(rw[i][j] & 0xFFFFu), rh = bf16_to_f32(rw[i][j] >> 16);
+        // new residual: the fp32 sum cast to bf16, as the pages write it
+        ro[j] = (uint32_t)f32_to_bf16(xl + rl) | ((uint32_t)f32_to_bf16(xh + rh) << 16);
+        const double sl = (double)xl + (double)rl, sh = (double)xh + (double)rh;
+        oo[j] = (uint32_t)f64_to_bf16((double)gg[2 * j] * (sl * rs)) |
+                ((uint32_t)f64_to_bf16((double)gg[2 * j + 1] * (sh * rs)) << 16);
       }
       *(uint4*)(res + t * d + c * 8) = make_uint4(ro[0], ro[1], ro[2], ro[3]);
       *(uint4*)(out + t * d + c * 8) = make_uint4(oo[0], oo[1], oo[2], oo[3]);

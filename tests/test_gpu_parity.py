@@ -236,9 +236,14 @@ def test_add_rmsnorm(T):
     torch.cuda.synchronize()
     assert np.array_equal(f64(res), res_ref)                    # new residual: bit-exact
     got = f64(out)
-    ulp = np.abs(hn_ref) * 2.0 ** -7
-    assert np.all(np.abs(got - hn_ref) <= ulp + 1e-30)          # within one bf16 ulp
-    assert np.mean(got == hn_ref) > 0.99
+    diff = np.flatnonzero(got != hn_ref)
+    if diff.size:
+        xv, rv = f64(x).ravel(), f64(res).ravel()
+        for i in diff[:8]:
+            print(f"[rmsnorm diff] idx={i} gpu={got.ravel()[i]!r} ref={hn_ref.ravel()[i]!r} "
+                  f"x={xv[i]!r} res={rv[i]!r}", flush=True)
+    print(f"[parity] add_rmsnorm T={T}: {diff.size} of {got.size} normalised values differ", flush=True)
+    assert np.array_equal(got, hn_ref)                          # normalised rows: bit-exact
 
 
 def test_add_rmsnorm_in_place_output():
@@ -385,3 +390,61 @@ def test_forward_full_skewed(full_params):
     _say("moe_forward full shape T=16384 Zipf bias (skewed)")
     bias = synth.gate_bias(synth.FULL, "zipf", DEV, seed=3, tag=1002)
     _full_case(full_params, bias, 16384, seed=103, n_random=3)
+
+
+# ----------------------------------------------------------------------------
+# stack of four blocks: fused residual-add RMSNorm + layer, residual in bf16
+# ----------------------------------------------------------------------------
+
+@pytest.mark.slow
+@pytest.mark.timeout(1200)
+def test_stack4_blocks_on_the_oracle_chain():
+    """Four independent full-shape blocks (fused residual-add RMSNorm + layer).
+
+    The oracle runs its own four-block chain on sampled tokens (its bf16 block
+    outputs feed its next block).  Each GPU block is then checked on exactly
+    the oracle's inputs of that block (x_b, residual_b) for those tokens -- the
+    layer is token-wise, so a token's result does not depend on the others in
+    the batch.  The new residual must be bit-exact, the update within the
+    layer's bounds.  (A free-running comparison is ill-conditioned: the
+    per-128 e4m3 requantisation of x and h turns the bf16-level differences of
+    one block's output into code flips in the next.  It is run and reported
+    below, not bounded.)
+    """
+    _say("stack of 4 blocks (full shape), oracle chain on sampled tokens")
+    data = synth.make_workload("stack4", device=DEV, tokens=1024)
+    dims = synth.FULL
+    cd = cdims(dims)
+    tok = np.array([3, 100, 257, 511, 640, 777, 901, 1023])
+    xs, rs = f64(data["x"])[tok], f64(data["residual"])[tok]
+    for b in range(4):
+        gain = data["gains"][b]
+        hv = HostView(data["blocks"][b])
+        hn, rs_new = oracle.add_rmsnorm(xs, rs, gain.cpu().numpy())
+        ref = oracle.moe_forward(hn, hv, dims)
+        # GPU block b on the oracle's block inputs
+        xg = torch.from_numpy(xs).to(torch.bfloat16).to(DEV)
+        rg = torch.from_numpy(rs).to(torch.bfloat16).to(DEV)
+        hg = torch.empty_like(xg)
+        moe.moe_add_rmsnorm(dims.d_model, tok.size, xg, rg, gain, 1e-6, hg)
+        gi = torch.empty((tok.size, dims.topk), dtype=torch.int32, device=DEV)
+        out = moe.MoELayer(cd, data["blocks"][b])(hg, idx=gi)
+        torch.cuda.synchronize()
+        assert np.array_equal(f64(rg), rs_new), f"block {b}: residual differs"
+        same, ndiff = routing_check(gi.cpu().numpy().astype(np.int64), ref["routing"], dims)
+        assert_close(f64(out)[same], ref["y"][same], f"stack block {b} on the oracle's inputs")
+        xs, rs = ref["delta"], rs_new                 # the oracle's own chain continues
+
+    # free-running GPU chain over all tokens: reported only
+    T = data["tokens"]
+    res = data["residual"].clone()
+    h = torch.empty_like(data["x"])
+    src = data["x"]
+    for b in range(4):
+        moe.moe_add_rmsnorm(dims.d_model, T, src, res, data["gains"][b], 1e-6, h)
+        src = moe.MoELayer(cd, data["blocks"][b])(h)
+    torch.cuda.synchronize()
+    mx, mean = metrics(f64(src)[tok], xs)
+    print(f"[report] free-running 4-block chain vs the oracle chain: max|d|/rms={mx:.3e} mean rel={mean:.3e}",
+          flush=True)
+    assert np.all(np.isfinite(f64(src)))
