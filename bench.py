@@ -67,6 +67,39 @@ class HipEvents:
         self.made = []
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ("mixture_experts_ffn_bias_amd/csrc/ffn.hip", "mixture_experts_ffn_bias_amd/csrc/common.h")
+
+
+def kernel_source_digest() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counters, or None.
+
+    profiles/traffic.json holds FETCH_SIZE and WRITE_SIZE (KiB per dispatch) per
+    workload and kernel, the factors that turn them into bytes (what the same
+    counters read for a plain device copy of known size) and the digest of the
+    kernel sources they were taken with; a different digest means the kernels
+    changed since, and no traffic is reported.
+    """
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    e = t.get("kernels", {}).get(f"{workload}/{kernel}")
+    if not e:
+        return None
+    return int((e["fetch_kib"] * t["fetch_factor"] + e["write_kib"] * t["write_factor"]) * 1024)
+
+
 def algorithmic_work(dims, T, touched):
     """Bytes and FLOPs each kernel must move / compute (implementation buffers excluded).
 
@@ -267,7 +300,7 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roof.update({"kernel": dom, "traffic": None, "launch_ms": round(stage_avg[dom], 4),
+    roof.update({"kernel": dom, "traffic": measured_traffic(args.workload, dom), "launch_ms": round(stage_avg[dom], 4),
                  "alg_bytes": int(bytes_per), "alg_flops": int(flops_per)})
 
     tokens = T * K

@@ -20,26 +20,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
                                                       int K, int d, uint16_t* __restrict__ delta) {
   __shared__ int s_row[32];
   __shared__ float s_w[32];
+  __shared__ int s_e[32];
   const int t = blockIdx.x;
   const int64_t TK = (int64_t)T * K;
-  if (threadIdx.x == 0) {
-    int ex[32];
-    for (int k = 0; k < K; ++k) {  // insertion sort by expert id
-      const int e = idx[(size_t)t * K + k];
-      int row = pair_row[(size_t)t * K + k];
-      row = row < 0 ? 0 : (row >= TK ? (int)(TK - 1) : row);
-      const float wk = w[(size_t)t * K + k];
-      int j = k;
-      while (j > 0 && ex[j - 1] > e) {
-        ex[j] = ex[j - 1];
-        s_row[j] = s_row[j - 1];
-        s_w[j] = s_w[j - 1];
-        --j;
-      }
-      ex[j] = e;
-      s_row[j] = row;
-      s_w[j] = wk;
+  // the token's K choices, loaded in parallel and placed by rank in ascending expert id
+  // (equal ids keep their order)
+  const int me = threadIdx.x;
+  int e = 0, row = 0;
+  float wk = 0.f;
+  if (me < K) {
+    e = idx[(size_t)t * K + me];
+    row = pair_row[(size_t)t * K + me];
+    row = row < 0 ? 0 : (row >= TK ? (int)(TK - 1) : row);
+    wk = w[(size_t)t * K + me];
+    s_e[me] = e;
+  }
+  __syncthreads();
+  if (me < K) {
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {
+      const int o = s_e[j];
+      rank += (o < e || (o == e && j < me)) ? 1 : 0;
     }
+    s_row[rank] = row;
+    s_w[rank] = wk;
   }
   __syncthreads();
   const int nch = d / 8;

@@ -89,8 +89,12 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
   return v > bv || (v == bv && i < bi);
 }
 
-// One wave per token, 4 tokens per 256-thread block.  Lane l holds experts
-// l, l+64, l+128, l+192.
+// WIDE = false: one wave per token, 4 tokens per 256-thread block; lane l
+// adds the K-split partial logits of experts l, l+64, l+128, l+192.
+// WIDE = true (many K splits, few tokens): one token per block; thread e adds
+// the partials of expert e, then all four waves run the selection on that
+// token and wave 0 writes it.
+template <bool WIDE>
 __global__ __launch_bounds__(256) void gate_select_kernel(const float* __restrict__ zpart, int ksplit,
                                                           const float* __restrict__ bias, int T, int E, int G,
                                                           int TG, int K, float route_scale,
@@ -102,52 +106,78 @@ __global__ __launch_bounds__(256) void gate_select_kernel(const float* __restric
   __shared__ int s_keep[4][64];
   __shared__ float s_sel[4][32];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  const bool live = t < T;
-  const int tt = live ? t : T - 1;
+  const int t = WIDE ? (int)blockIdx.x : (int)blockIdx.x * 4 + wave;
+  const bool live = t < T && (!WIDE || wave == 0);
+  const int tt = t < T ? t : T - 1;
   const int epg = E / G;
-
-  // logits: the K-split partial sums, added in split order; eight splits of
-  // all four experts are loaded before they are added
-  float z[4] = {0.f, 0.f, 0.f, 0.f};
-  const float* zp = zpart + (size_t)tt * E + lane;
+  const int slot = WIDE ? 0 : wave;  // LDS row of the token's scores
   const size_t split_stride = (size_t)T * E;
-  int ks = 0;
-  for (; ks + 8 <= ksplit; ks += 8) {
-    float v[8][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[j][i] = (lane + 64 * i < E) ? zp[(ks + j) * split_stride + 64 * i] : 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) z[i] += v[j][i];
-  }
-  for (; ks < ksplit; ++ks)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) z[i] += zp[ks * split_stride + 64 * i];
 
+  if (WIDE) {
+    // logits: the K-split partial sums, added in split order, eight loads in flight
+    const int e = threadIdx.x;
+    if (e < E) {
+      const float* zp = zpart + (size_t)tt * E + e;
+      float z = 0.f;
+      int ks = 0;
+      for (; ks + 8 <= ksplit; ks += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = zp[(ks + j) * split_stride];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) z += v[j];
+      }
+      for (; ks < ksplit; ++ks) z += zp[ks * split_stride];
+      const float s = 1.f / (1.f + expf(-z));
+      float v = s + bias[e];
+      if (v != v) v = -INFINITY;  // NaN never wins a comparison below
+      s_score[0][e] = s;
+      s_biased[0][e] = v;
+    }
+  } else {
+    // logits: the K-split partial sums, added in split order; eight splits of
+    // all four experts are loaded before they are added
+    float z[4] = {0.f, 0.f, 0.f, 0.f};
+    const float* zp = zpart + (size_t)tt * E + lane;
+    int ks = 0;
+    for (; ks + 8 <= ksplit; ks += 8) {
+      float v[8][4];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[j][i] = (lane + 64 * i < E) ? zp[(ks + j) * split_stride + 64 * i] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) z[i] += v[j][i];
+    }
+    for (; ks < ksplit; ++ks)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i < E) z[i] += zp[ks * split_stride + 64 * i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E) {
+        const float s = 1.f / (1.f + expf(-z[i]));
+        float v = s + bias[e];
+        if (v != v) v = -INFINITY;
+        s_score[wave][e] = s;
+        s_biased[wave][e] = v;
+      }
+    }
+  }
+  __syncthreads();
   float b[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    b[i] = -INFINITY;
-    if (e < E) {
-      const float s = 1.f / (1.f + expf(-z[i]));
-      float v = s + bias[e];
-      if (v != v) v = -INFINITY;  // NaN never wins a comparison below
-      s_score[wave][e] = s;
-      s_biased[wave][e] = v;
-      b[i] = v;
-    }
+    b[i] = e < E ? s_biased[slot][e] : -INFINITY;
   }
-  __syncthreads();
   if (lane < G) {  // group score: sum of the two largest biased scores
     float m1 = -INFINITY, m2 = -INFINITY;
     for (int j = 0; j < epg; ++j) {
-      const float v = s_biased[wave][lane * epg + j];
+      const float v = s_biased[slot][lane * epg + j];
       if (v > m1) {
         m2 = m1;
         m1 = v;
@@ -203,7 +233,7 @@ __global__ __launch_bounds__(256) void gate_select_kernel(const float* __restric
     for (int i = 0; i < 4; ++i)
       if (bi == lane + 64 * i) avail[i] = false;
     if (lane == 0) {
-      s_sel[wave][k] = s_score[wave][bi];
+      s_sel[wave][k] = s_score[slot][bi];
       if (live) idx_out[(size_t)t * K + k] = bi;
     }
   }
@@ -238,8 +268,12 @@ hipError_t launch_gate(const uint16_t* x, const float* gate_w, const float* gate
   hipLaunchKernelGGL(gate_logits_kernel, grid, dim3(256), 0, s, x, gate_w, zpart, T, d, E, kchunk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(gate_select_kernel, dim3((T + 3) / 4), dim3(256), 0, s, zpart, kz, gate_b, T, E, G, TG, K,
-                     route_scale, idx, w);
+  if (kz >= 8 && T <= 1024)
+    hipLaunchKernelGGL(gate_select_kernel<true>, dim3(T), dim3(256), 0, s, zpart, kz, gate_b, T, E, G, TG, K,
+                       route_scale, idx, w);
+  else
+    hipLaunchKernelGGL(gate_select_kernel<false>, dim3((T + 3) / 4), dim3(256), 0, s, zpart, kz, gate_b, T, E, G,
+                       TG, K, route_scale, idx, w);
   return hipGetLastError();
 }
 

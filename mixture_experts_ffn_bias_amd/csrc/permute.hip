@@ -100,13 +100,10 @@ __global__ __launch_bounds__(PERM_CHUNK) void scatter_kernel(const int32_t* __re
 
 // Per-128-block e4m3 quantisation of bf16 rows: 8 lanes per block, 16
 // elements per lane.  scale = amax / 448 (correctly rounded fp32 division),
-// code = e4m3_rne(v / scale); an all-zero block gets scale 1.
-__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
-                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t blk = gid >> 3;
-  const int sub = (int)(gid & 7);
-  if (blk >= nblocks) return;  // whole 8-lane groups leave together
+// code = e4m3_rne(v / scale); an all-zero block gets scale 1.  The 8 lanes
+// of a block are consecutive lanes of one wave and call this together.
+__device__ __forceinline__ void quant_block(const uint16_t* __restrict__ x, int64_t blk, int sub,
+                                            uint8_t* __restrict__ q, float* __restrict__ scale) {
   const uint4* p = (const uint4*)(x + blk * BLK + sub * 16);
   const uint4 u0 = p[0], u1 = p[1];
   const uint32_t w[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
@@ -131,12 +128,81 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
   if (sub == 0) scale[blk] = sc;
 }
 
+__global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t blk = gid >> 3;
+  if (blk >= nblocks) return;  // whole 8-lane groups leave together
+  quant_block(x, blk, (int)(gid & 7), q, scale);
+}
+
+// Everything for T <= PERM_CHUNK in one launch: block 0 counts, scans and
+// scatters (one chunk, masks kept in LDS); blocks 1.. quantise x.
+__global__ __launch_bounds__(PERM_CHUNK) void permute_small_kernel(
+    const int32_t* __restrict__ idx, int T, int K, int E, int32_t* __restrict__ counts,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ pair_row,
+    const uint16_t* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ q, float* __restrict__ scale) {
+  if (blockIdx.x > 0) {
+    const int64_t gid = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
+    const int64_t blk = gid >> 3;
+    if (blk < nblocks) quant_block(x, blk, (int)(gid & 7), q, scale);
+    return;
+  }
+  __shared__ uint32_t mask[256 * MASK_WORDS];
+  __shared__ int s[256];
+  __shared__ int s_off[256];
+  build_masks(mask, idx, T, K, E);
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E) {
+#pragma unroll
+    for (int j = 0; j < MASK_WORDS; ++j) cnt += __popc(mask[e * MASK_WORDS + j]);
+  }
+  s[e] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const int v = e >= o ? s[e - o] : 0;
+    __syncthreads();
+    s[e] += v;
+    __syncthreads();
+  }
+  s_off[e] = s[e] - cnt;
+  if (e < E) {
+    counts[e] = cnt;
+    offsets[e] = s[e] - cnt;
+  }
+  if (e == 255) offsets[E] = s[255];
+  __syncthreads();
+  const int t = threadIdx.x;
+  if (t < T) {
+    const int w = t >> 5;
+    const uint32_t below = (1u << (t & 31)) - 1u;
+    for (int k = 0; k < K; ++k) {
+      const int ek = clamp_expert(idx[(size_t)t * K + k], E);
+      const uint32_t* m = mask + ek * MASK_WORDS;
+      int rank = __popc(m[w] & below);
+      for (int j = 0; j < w; ++j) rank += __popc(m[j]);
+      const int pos = s_off[ek] + rank;
+      row_token[pos] = t;
+      pair_row[(size_t)t * K + k] = pos;
+    }
+    row_token[(size_t)T * K + t] = t;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, int E, int K, int32_t* chunk_cnt,
                           int32_t* chunk_off, int32_t* counts, int32_t* offsets, int32_t* row_token,
                           int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s) {
   const int nchunks = (T + PERM_CHUNK - 1) / PERM_CHUNK;
+  if (nchunks == 1) {
+    const int64_t nblocks = (int64_t)T * (d / BLK);
+    const int64_t qblocks = (nblocks * 8 + PERM_CHUNK - 1) / PERM_CHUNK;
+    hipLaunchKernelGGL(permute_small_kernel, dim3((unsigned)(1 + qblocks)), dim3(PERM_CHUNK), 0, s, idx, T, K, E,
+                       counts, offsets, row_token, pair_row, x, nblocks, xq, xs);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(count_kernel, dim3(nchunks), dim3(PERM_CHUNK), 0, s, idx, T, K, E, chunk_cnt);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
