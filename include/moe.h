@@ -20,7 +20,7 @@
  *  - bf16 tensors are passed as uint16_t (the bit pattern).  FP8 tensors are
  *    OCP e4m3fn codes (uint8_t), with one float32 scale per 128x128 block.
  *  - Row-major layouts throughout.  d_model and inter must be multiples of
- *    128 and at most 16384; n_experts <= 256 and a multiple of 16; experts
+ *    128 and at most 32768; n_experts <= 256 and a multiple of 16; experts
  *    per group >= 2; n_groups <= 64; topk <= 32.
  *  - Errors: arguments are checked on the host before anything is enqueued;
  *    a negative moe_status is returned and nothing runs.  A failed launch
@@ -174,6 +174,24 @@ int moe_forward_timed(const moe_dims* dims, const moe_weights* weights, int64_t 
  * d must be a multiple of 128 and at most 16384.  No workspace. */
 int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* residual,
                     const float* gain, float eps, uint16_t* out, void* stream);
+
+/* Workspace bytes moe_mlp needs for `tokens` tokens.  Returns 0 for invalid sizes. */
+size_t moe_mlp_workspace_size(int32_t d_model, int32_t inter, int64_t tokens);
+
+/* Dense MLP of the blocks that precede the MoE blocks ("DeepSeek-V3.2-Exp ·
+ * MoE update", block excerpt: the first n_dense_layers blocks build
+ * MLP(dim, inter_dim) where the others build the MoE).  The pages print
+ * neither the MLP's body nor inter_dim; it is taken to be the SwiGLU of one
+ * expert in the same FP8 form ("Gate projection", expert and Linear excerpts):
+ *   out[t] = bf16(Q(h) . W2^T),  h = bf16(silu(bf16(Q(x[t]) . W1^T)) * bf16(Q(x[t]) . W3^T))
+ * with Q the per-128-block e4m3 activation quantiser of moe_grouped_ffn.
+ *   mlp   one expert's weights (n = 1): w1, w3 [inter][d_model], w2 [d_model][inter]
+ *   x     bf16 [T][d_model] (16-byte aligned)
+ *   out   bf16 [T][d_model] out (16-byte aligned; must not alias x)
+ * d_model and inter: multiples of 128, at most 32768.  Needs
+ * moe_mlp_workspace_size(d_model, inter, T) bytes of workspace (256-byte aligned). */
+int moe_mlp(int32_t d_model, int32_t inter, int64_t tokens, const moe_experts* mlp, const uint16_t* x,
+            uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Static description of a status code. */
 const char* moe_status_string(int status);

@@ -6,6 +6,6 @@ package is its Python binding.
 """
 from ._binding import (  # noqa: F401
     LIB_PATH, MOE_FORWARD_EVENTS, SYMBOLS, MoeError, MoELayer, experts_struct, lib, make_dims, moe_add_rmsnorm, moe_combine,
-    moe_dims, moe_experts, moe_forward, moe_forward_timed, moe_gate, moe_grouped_ffn, moe_permute, moe_weights, moe_workspace_size,
-    status_string, workspace,
+    moe_dims, moe_experts, moe_forward, moe_forward_timed, moe_gate, moe_grouped_ffn, moe_mlp, moe_mlp_workspace_size,
+    moe_permute, moe_weights, moe_workspace_size, mlp_workspace, status_string, workspace,
 )

@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK = 0
 SYMBOLS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-           "moe_forward_timed", "moe_add_rmsnorm", "moe_status_string")
+           "moe_forward_timed", "moe_add_rmsnorm", "moe_mlp_workspace_size", "moe_mlp", "moe_status_string")
 MOE_FORWARD_EVENTS = 6
 
 
@@ -66,8 +66,11 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_timed.argtypes = [dp, ctypes.POINTER(moe_weights), i64, vp, vp, vp, vp, vp, sz, vp,
                                         ctypes.POINTER(ctypes.c_void_p)]
         L.moe_add_rmsnorm.argtypes = [i32, i64, vp, vp, vp, ctypes.c_float, vp, vp]
+        L.moe_mlp_workspace_size.argtypes = [i32, i32, i64]
+        L.moe_mlp_workspace_size.restype = sz
+        L.moe_mlp.argtypes = [i32, i32, i64, ctypes.POINTER(moe_experts), vp, vp, vp, sz, vp]
         for n in ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
-                  "moe_add_rmsnorm"):
+                  "moe_add_rmsnorm", "moe_mlp"):
             getattr(L, n).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -160,6 +163,22 @@ def moe_forward_timed(dims, weights: moe_weights, tokens, x, delta, idx_out, w_o
 def moe_add_rmsnorm(d, tokens, x, residual, gain, eps, out, stream=None):
     _check(lib().moe_add_rmsnorm(int(d), int(tokens), _p(x), _p(residual), _p(gain), float(eps), _p(out),
                                  _stream(stream)), "moe_add_rmsnorm")
+
+
+def moe_mlp_workspace_size(d_model: int, inter: int, tokens: int) -> int:
+    return int(lib().moe_mlp_workspace_size(int(d_model), int(inter), int(tokens)))
+
+
+def mlp_workspace(d_model: int, inter: int, tokens: int, device="cuda") -> torch.Tensor:
+    n = moe_mlp_workspace_size(d_model, inter, tokens)
+    if n == 0 and tokens > 0:
+        raise MoeError(-1, "moe_mlp_workspace_size")
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def moe_mlp(d_model, inter, tokens, mlp: moe_experts, x, out, ws, stream=None):
+    _check(lib().moe_mlp(int(d_model), int(inter), int(tokens), ctypes.byref(mlp), _p(x), _p(out), _p(ws),
+                         ws.numel() if ws is not None else 0, _stream(stream)), "moe_mlp")
 
 
 _EXPERT_KEYS = ("w1", "w3", "w2", "s1", "s3", "s2")

@@ -12,6 +12,7 @@ using namespace moe;
 namespace {
 
 constexpr size_t WS_ALIGN = 256;
+constexpr int MAX_FEATURES = 32768;  // 256 K blocks per projection in the tiled FFN kernels
 
 struct Layout {
   size_t zpart, idx, w, chunk_cnt, chunk_off, counts, offsets, row_token, pair_row, tiles, n_tiles, xq, xs, hq,
@@ -52,6 +53,37 @@ Layout layout(const moe_dims& dm, int64_t T) {
   return L;
 }
 
+// Dense MLP: xq, xs, the tile list and h.
+struct MlpLayout {
+  size_t xq, xs, tiles, n_tiles, hq, hs, total;
+};
+
+MlpLayout mlp_layout(int d, int I, int64_t T) {
+  MlpLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t t = (size_t)T;
+  L.xq = take(t * d);
+  L.xs = take(t * (d / BLK) * 4);
+  L.tiles = take((size_t)ffn_max_tiles(T, 0, 0, ffn_tile_rows(T)) * sizeof(int4));
+  L.n_tiles = take(4);
+  L.hq = take(t * I);
+  L.hs = take(t * (I / BLK) * 4);
+  L.total = off;
+  return L;
+}
+
+int check_mlp(int32_t d, int32_t I, int64_t T) {
+  if (d <= 0 || I <= 0 || T < 0) return MOE_ERR_INVALID_ARG;
+  if (d % BLK != 0 || I % BLK != 0 || d > MAX_FEATURES || I > MAX_FEATURES) return MOE_ERR_UNSUPPORTED;
+  if (T > 0x7fffffff) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 int check_dims(const moe_dims* p) {
   if (!p) return MOE_ERR_INVALID_ARG;
   const moe_dims& d = *p;
@@ -61,7 +93,7 @@ int check_dims(const moe_dims* p) {
   if (d.topk > d.topk_groups * (d.n_experts / d.n_groups)) return MOE_ERR_INVALID_ARG;
   if (!isfinite(d.route_scale)) return MOE_ERR_INVALID_ARG;
   if (d.d_model % BLK != 0 || d.inter % BLK != 0) return MOE_ERR_UNSUPPORTED;
-  if (d.d_model > 16384 || d.inter > 16384) return MOE_ERR_UNSUPPORTED;  // at most 128 K blocks per projection
+  if (d.d_model > MAX_FEATURES || d.inter > MAX_FEATURES) return MOE_ERR_UNSUPPORTED;
   if (d.n_experts > 256 || d.n_experts % 16 != 0) return MOE_ERR_UNSUPPORTED;
   if (d.n_groups > 64 || d.n_experts / d.n_groups < 2) return MOE_ERR_UNSUPPORTED;
   if (d.topk > 32) return MOE_ERR_UNSUPPORTED;
@@ -264,6 +296,32 @@ int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* resi
   if (!x || !residual || !gain || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(residual, 16) || !aligned(gain, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
   return hip_status(launch_add_rmsnorm(x, residual, gain, eps, d, tokens, out, (hipStream_t)stream));
+}
+
+size_t moe_mlp_workspace_size(int32_t d_model, int32_t inter, int64_t tokens) {
+  if (check_mlp(d_model, inter, tokens) != MOE_OK) return 0;
+  return mlp_layout(d_model, inter, tokens).total;
+}
+
+int moe_mlp(int32_t d_model, int32_t inter, int64_t tokens, const moe_experts* mlp, const uint16_t* x,
+            uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_mlp(d_model, inter, tokens));
+  if (tokens == 0) return MOE_OK;
+  MOE_TRY(check_experts(mlp));
+  if (!x || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16)) return MOE_ERR_ALIGN;
+  const MlpLayout L = mlp_layout(d_model, inter, tokens);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  uint8_t* xq = at<uint8_t>(workspace, L.xq);
+  float* xs = at<float>(workspace, L.xs);
+  MOE_TRY(hip_status(launch_quant(x, tokens, d_model, xq, xs, s)));
+  // one dense expert: no routed experts, rows are tokens
+  const ExpertPtrs p = ptrs(*mlp);
+  return hip_status(launch_ffn(p, &p, (int)tokens, d_model, inter, 0, 0, nullptr, nullptr, xq, xs,
+                               at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
+                               at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), out, s));
 }
 
 const char* moe_status_string(int status) {

@@ -26,6 +26,11 @@ constexpr int64_t STREAM_MAX_TOKENS = 128;
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// token of permuted row `row` (NULL map: rows are tokens, as for a dense MLP)
+__device__ __forceinline__ int token_of(const int32_t* row_token, int row, int T) {
+  return row_token ? clampi(row_token[row], 0, T - 1) : row;
+}
+
 // One block of 256 threads.  tiles[i] = {expert, first row, rows, 0}; the
 // shared expert is expert E with rows [T*K, T*K + T).
 __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restrict__ offsets, int E, int T, int K,
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(512) void ffn_up_stream_kernel(FfnArgs a) {
   const uint8_t* a3 = Pp.w3 + (eo * a.I + o) * (size_t)a.d;
   const float* s1 = Pp.s1 + (eo * nib + ib) * nkb;
   const float* s3 = Pp.s3 + (eo * nib + ib) * nkb;
-  const int tok = clampi(a.row_token[row0 + min(r, nrows - 1)], 0, a.T - 1);
+  const int tok = token_of(a.row_token, row0 + min(r, nrows - 1), a.T);
   const uint8_t* bq = a.xq + (size_t)tok * a.d;
   const float* bs = a.xs + (size_t)tok * nkb;
 
@@ -252,7 +257,7 @@ constexpr int TT_S_BYTES = TT_ROWS * 4;      // activation scales of one K block
 constexpr int TT_STAGE = TT_A_BYTES + TT_B_BYTES + TT_S_BYTES;
 constexpr int TT_NSTAGE = 3;
 constexpr int TT_SMEM = TT_NSTAGE * TT_STAGE;
-constexpr int TT_MAX_KB = 128;               // K blocks per projection the tiled kernels support
+constexpr int TT_MAX_KB = 256;               // K blocks per projection the tiled kernels support
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -449,11 +454,11 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
         return base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d;
       },
       [&](int row) {
-        const int tok = clampi(rt[row0 + min(row, nrows - 1)], 0, a.T - 1);
+        const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T);
         return a.xq + (size_t)tok * a.d;
       },
       [&](int row) {
-        const int tok = clampi(rt[row0 + min(row, nrows - 1)], 0, a.T - 1);
+        const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T);
         return a.xs + (size_t)tok * nkb;
       });
   const float* sa[2] = {P.s1 + (eo * nib + ib) * nkb, P.s3 + (eo * nib + ib) * nkb};

@@ -29,10 +29,14 @@ hipError_t launch_gate(const uint16_t* x, const float* gate_w, const float* gate
 hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, int E, int K,
                           int32_t* chunk_cnt, int32_t* chunk_off, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s);
+// per-128-block e4m3 quantisation of T rows of d bf16 values
+hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s);
 
 // ffn.hip
 int ffn_tile_rows(int64_t T);                       // rows per FFN tile for this token count
 int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
+// E = K = 0 with `shared` set and row_token NULL runs one dense expert over
+// rows 0..T-1 (offsets is then not read).
 // ev: NULL, or three events recorded before the up-projection, before the
 // down-projection and after it (the tile plan precedes ev[0]).
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E,

@@ -192,6 +192,13 @@ __global__ __launch_bounds__(PERM_CHUNK) void permute_small_kernel(
 
 }  // namespace
 
+hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s) {
+  const int64_t nblocks = T * (d / BLK);
+  const int64_t threads = nblocks * 8;
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, nblocks, xq, xs);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, int E, int K, int32_t* chunk_cnt,
                           int32_t* chunk_off, int32_t* counts, int32_t* offsets, int32_t* row_token,
                           int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s) {
@@ -211,10 +218,7 @@ hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, i
   hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(PERM_CHUNK), 0, s, idx, T, K, E, chunk_off, offsets,
                      row_token, pair_row);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  const int64_t nblocks = (int64_t)T * (d / BLK);
-  const int64_t threads = nblocks * 8;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, nblocks, xq, xs);
-  return hipGetLastError();
+  return launch_quant(x, T, d, xq, xs, s);
 }
 
 }  // namespace moe

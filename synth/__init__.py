@@ -146,6 +146,12 @@ def make_block(dims: Dims, bias_law: str, device, seed: int, block: int = 0) -> 
     return p
 
 
+def mlp_weights(d_model: int, inter: int, device, seed: int) -> Dict[str, torch.Tensor]:
+    """One dense SwiGLU MLP (d_model -> inter -> d_model) in the experts' FP8 form, leading dim 1."""
+    dims = Dims(d_model=d_model, n_experts=1, n_groups=1, topk_groups=1, topk=1, inter=inter)
+    return expert_weights(dims, 1, device, seed, 500)
+
+
 def make_x(dims: Dims, tokens: int, device, seed: int, tag: int = 1) -> torch.Tensor:
     return _normal((tokens, dims.d_model), 1.0, device, seed, tag).to(torch.bfloat16)
 

@@ -93,6 +93,7 @@ def test_zero_tokens_is_a_noop_everywhere():
     assert L.moe_combine(d, 0, None, None, None, None, 1, None, None) == 0
     assert L.moe_forward(d, None, 0, None, None, None, None, None, 0, None) == 0
     assert L.moe_add_rmsnorm(7168, 0, None, None, None, 1e-6, None, None) == 0
+    assert L.moe_mlp(7168, 18432, 0, None, None, None, None, 0, None) == 0
 
 
 def test_null_pointers_rejected():
@@ -135,3 +136,24 @@ def test_python_binding_raises_on_error_codes():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_gate(dims(topk_groups=9), 4, FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert ei.value.code == -1
+
+
+def test_mlp_argument_checks():
+    L = B.lib()
+    ex = moe.moe_experts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    need = moe.moe_mlp_workspace_size(7168, 18432, 64)
+    # xq + xs + h, at least
+    assert need >= 64 * 7168 + 64 * 56 * 4 + 64 * 18432
+    assert moe.moe_mlp_workspace_size(7168, 18432 + 64, 64) == 0
+    assert moe.moe_mlp_workspace_size(7168, 32768 + 128, 64) == 0
+    assert moe.moe_mlp_workspace_size(0, 2048, 64) == 0
+    assert L.moe_mlp(7168, 18432 + 64, 64, ctypes.byref(ex), FAKE, FAKE, FAKE, 1 << 30, None) == -2
+    assert L.moe_mlp(-128, 2048, 64, ctypes.byref(ex), FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_mlp(7168, 2048, -1, ctypes.byref(ex), FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_mlp(7168, 2048, 64, None, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_mlp(7168, 2048, 64, ctypes.byref(ex), None, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_mlp(7168, 2048, 64, ctypes.byref(ex), FAKE + 2, FAKE, FAKE, 1 << 30, None) == -4
+    assert L.moe_mlp(7168, 2048, 64, ctypes.byref(ex), FAKE, FAKE, FAKE + 16, 1 << 30, None) == -4
+    small = moe.moe_mlp_workspace_size(7168, 2048, 64)
+    assert L.moe_mlp(7168, 2048, 64, ctypes.byref(ex), FAKE, FAKE, FAKE, small - 1, None) == -3
+    assert L.moe_mlp(7168, 2048, 64, ctypes.byref(ex), FAKE, FAKE, None, small, None) == -3

@@ -448,3 +448,50 @@ def test_stack4_blocks_on_the_oracle_chain():
     print(f"[report] free-running 4-block chain vs the oracle chain: max|d|/rms={mx:.3e} mean rel={mean:.3e}",
           flush=True)
     assert np.all(np.isfinite(f64(src)))
+
+
+# ----------------------------------------------------------------------------
+# dense MLP (the blocks before the MoE blocks)
+# ----------------------------------------------------------------------------
+
+def run_mlp(p, x, d, inter):
+    T = x.shape[0]
+    out = torch.full((T, d), float("nan"), dtype=torch.bfloat16, device=DEV)
+    ws = moe.mlp_workspace(d, inter, T)
+    mlp = moe.experts_struct(*(p[k] for k in ("w1", "w3", "w2", "s1", "s3", "s2")))
+    moe.moe_mlp(d, inter, T, mlp, x, out, ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def _mlp_ref(pn, xv):
+    return oracle.expert_ffn(xv, pn["w1"][0], pn["s1"][0], pn["w3"][0], pn["s3"][0], pn["w2"][0], pn["s2"][0])
+
+
+@pytest.mark.parametrize("T", [1, 37, 128, 129, 300])
+def test_mlp_tiny(T):
+    d, inter = 512, 384
+    _say(f"moe_mlp d={d} inter={inter} T={T}")
+    p = synth.mlp_weights(d, inter, DEV, seed=7)
+    x = synth.make_x(synth.Dims(d, 1, 1, 1, 1, inter), T, DEV, seed=70 + T)
+    got = f64(run_mlp(p, x, d, inter))
+    assert_rows_close(got, _mlp_ref(_np_params(p), f64(x)), f"mlp tiny T={T}")
+
+
+@pytest.mark.slow
+@pytest.mark.parametrize("T", [64, 1000])
+def test_mlp_full_width_sampled_rows(T):
+    # d = 7168 (the pages' model width); inter = 18432, a width the pages leave open, chosen
+    # because it needs 144 K blocks in the down-projection
+    d, inter = 7168, 18432
+    _say(f"moe_mlp d={d} inter={inter} T={T}")
+    p = synth.mlp_weights(d, inter, DEV, seed=8)
+    x = synth.make_x(synth.Dims(d, 1, 1, 1, 1, inter), T, DEV, seed=80 + T)
+    got = f64(run_mlp(p, x, d, inter))
+    # first, last and tile-edge rows plus a seeded sample
+    rng = np.random.default_rng(T)
+    edges = [0, 1, 15, 16, 127, 128, T - 1]
+    rows = np.unique(np.concatenate([[r for r in edges if r < T], rng.choice(T, min(T, 16), replace=False)]))
+    ref = _mlp_ref(_np_params(p), f64(x)[rows])
+    assert_rows_close(got[rows], ref, f"mlp full-width T={T}")
+    assert np.isfinite(got).all()
