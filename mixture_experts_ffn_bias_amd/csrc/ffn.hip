@@ -3,11 +3,13 @@
 // ``w2((silu(w1(x).float()) * w3(x).float()).type_as(x))`` and Linear excerpt:
 // FP8 weights [out, in] with one fp32 scale per 128x128 block).
 //
-// Work unit ("tile"): up to 16*MT consecutive permuted rows of one expert.
-// Up-projection workgroups own (tile, 128-column block of h): the 8 waves
-// each compute 16 h columns from the matching 16 rows of w1 and of w3, so
-// the workgroup holds the whole 128-wide block and quantises h to e4m3 in its
-// epilogue.  Down-projection workgroups own (tile, 128 output features).
+// Work unit ("tile"): up to 16 (streaming kernels, T <= 128) or 128 (tiled
+// kernels) consecutive permuted rows of one expert.  Up-projection
+// workgroups own (tile, 128-column block of h) and hold the w1 and w3 rows of
+// that block, so the whole 128-wide block of h is in one workgroup, which
+// applies SwiGLU and quantises h to e4m3 in its epilogue.  Down-projection
+// workgroups own (tile, 128 output features) (streaming) or (tile, 256 output
+// features) (tiled).
 //
 // Each 128-deep scale block is one block_dot (four bf16 MFMAs on exactly
 // decoded e4m3 operands), so each block sum is scaled once:
@@ -242,11 +244,13 @@ __global__ __launch_bounds__(512) void ffn_down_stream_kernel(FfnArgs a) {
 //                    in the same lane and the epilogue fuses SwiGLU + h quant);
 //   down-projection: two consecutive 128-feature blocks of w2.
 // Per 128-deep K block, the e4m3 weight (256 x 128 B) and activation
-// (128 x 128 B) tiles are staged in LDS with 144-byte rows (the 16-byte pad
-// makes the MFMA-layout reads bank-conflict free), double buffered, with the
-// global loads issued two K blocks ahead.  Wave (wr, wc) multiplies rows
-// [64 wr, 64 wr + 64) by weight rows {32 wc .. 32 wc + 31} of both groups:
-// 4 x 4 block products per K block.
+// (128 x 128 B) tiles and the activation scales are copied global -> LDS
+// directly (global_load_lds, no register staging) into one of three stage
+// buffers, two K blocks ahead of the multiply.  Rows are stored unpadded with
+// their 16-byte chunks XOR-permuted (swz), which makes the MFMA-layout reads
+// bank-conflict free.  Wave (wr, wc) multiplies rows [64 wr, 64 wr + 64) by
+// weight rows {32 wc .. 32 wc + 31} of both groups: 4 x 4 block products per
+// K block.
 // ---------------------------------------------------------------------------
 
 constexpr int TT_ROWS = 128;                 // activation rows per tile
