@@ -69,16 +69,6 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)v;
 }
 
-// The 32 bytes one lane contributes to an e4m3 MFMA operand for K block
-// `p` (128 bytes): chunks [16g, 16g+16) and [64+16g, 64+16g+16), g = lane/16.
-// Each load instruction of a wave then covers 64 contiguous bytes per row.
-__device__ __forceinline__ v8i load_frag_e4m3(const uint8_t* row_k, int g) {
-  v4i lo = *(const v4i*)(row_k + 16 * g);
-  v4i hi = *(const v4i*)(row_k + 64 + 16 * g);
-  v8i r = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-  return r;
-}
-
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

@@ -3,13 +3,11 @@
 // ``w2((silu(w1(x).float()) * w3(x).float()).type_as(x))`` and Linear excerpt:
 // FP8 weights [out, in] with one fp32 scale per 128x128 block).
 //
-// Work unit ("tile"): up to 16 (streaming kernels, T <= 128) or 128 (tiled
-// kernels) consecutive permuted rows of one expert.  Up-projection
-// workgroups own (tile, 128-column block of h) and hold the w1 and w3 rows of
-// that block, so the whole 128-wide block of h is in one workgroup, which
-// applies SwiGLU and quantises h to e4m3 in its epilogue.  Down-projection
-// workgroups own (tile, 128 output features) (streaming) or (tile, 256 output
-// features) (tiled).
+// Work unit ("tile"): up to 128 consecutive permuted rows of one expert.
+// Up-projection workgroups own (tile, 128-column block of h) and hold the w1
+// and w3 rows of that block, so the whole 128-wide block of h is in one
+// workgroup, which applies SwiGLU and quantises h to e4m3 in its epilogue.
+// Down-projection workgroups own (tile, 256 output features).
 //
 // Each 128-deep scale block is one block_dot (four bf16 MFMAs on exactly
 // decoded e4m3 operands), so each block sum is scaled once:
@@ -23,9 +21,6 @@ namespace moe {
 
 namespace {
 
-constexpr int STREAM_DEPTH = 4;          // K-blocks in flight per wave in the streaming kernels
-constexpr int64_t STREAM_MAX_TOKENS = 128;
-
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // token of permuted row `row` (NULL map: rows are tokens, as for a dense MLP)
@@ -33,14 +28,20 @@ __device__ __forceinline__ int token_of(const int32_t* row_token, int row, int T
   return row_token ? clampi(row_token[row], 0, T - 1) : row;
 }
 
-// One block of 256 threads.  tiles[i] = {expert, first row, rows, 0}; the
-// shared expert is expert E with rows [T*K, T*K + T).
+// One block of 256 threads.  tiles[i] = {expert, first row, rows, once}; the
+// shared expert is expert E with rows [T*K, T*K + T).  once = 1 when the tile
+// is the only one of its expert, so its weights are read exactly once.  The
+// shared expert's tiles come first: they hold the most rows when T is small,
+// and starting the longest work first keeps it off the end of the launch.
 __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restrict__ offsets, int E, int T, int K,
                                                          int NT, int has_shared, int cap,
                                                          int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
   __shared__ int s[256];
   const int e = threadIdx.x;
   const int TK = T * K;
+  const int nsh = has_shared ? (T + NT - 1) / NT : 0;
+  for (int j = threadIdx.x; j < nsh; j += blockDim.x)
+    tiles[j] = make_int4(E, TK + j * NT, min(NT, T - j * NT), nsh == 1 ? 1 : 0);
   int lo = 0, cnt = 0, n = 0;
   if (e < E) {
     lo = clampi(offsets[e], 0, TK);
@@ -57,17 +58,9 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
     __syncthreads();
   }
   const int base = s[e] - n;
-  const int routed = min(s[255], cap);
   for (int j = 0; j < n && base + j < cap; ++j)
-    tiles[base + j] = make_int4(e, lo + j * NT, min(NT, cnt - j * NT), 0);
-  int total = routed;
-  if (has_shared) {
-    const int nsh = (T + NT - 1) / NT;
-    for (int j = threadIdx.x; j < nsh; j += blockDim.x)
-      tiles[routed + j] = make_int4(E, TK + j * NT, min(NT, T - j * NT), 0);
-    total += nsh;
-  }
-  if (threadIdx.x == 0) *n_tiles = total;
+    tiles[nsh + base + j] = make_int4(e, lo + j * NT, min(NT, cnt - j * NT), n == 1 ? 1 : 0);
+  if (threadIdx.x == 0) *n_tiles = nsh + min(s[255], cap);
 }
 
 struct FfnArgs {
@@ -85,160 +78,8 @@ struct FfnArgs {
 };
 
 // ---------------------------------------------------------------------------
-// Streaming variants for small batches (every tile <= 16 rows): the weights
-// are read once from HBM and dominate the traffic, so each wave keeps P
-// K-blocks of raw e4m3 fragments (weights, activations, activation scales)
-// in flight in a register ring and issues the loads for block kb+P before it
-// decodes and multiplies block kb.
-// ---------------------------------------------------------------------------
-
-template <int P>
-__global__ __launch_bounds__(512) void ffn_up_stream_kernel(FfnArgs a) {
-  const int nib = a.I / BLK, nkb = a.d / BLK;
-  const int tile = blockIdx.x / nib, ib = blockIdx.x - tile * nib;
-  if (tile >= *a.n_tiles) return;  // uniform for the whole block, before any barrier
-  const int4 td = a.tiles[tile];
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const bool sh = e >= a.E;
-  const ExpertPtrs& Pp = sh ? a.shared : a.routed;
-  const size_t eo = sh ? 0 : (size_t)e;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int o = ib * BLK + 16 * wave + r;
-  const uint8_t* a1 = Pp.w1 + (eo * a.I + o) * (size_t)a.d;
-  const uint8_t* a3 = Pp.w3 + (eo * a.I + o) * (size_t)a.d;
-  const float* s1 = Pp.s1 + (eo * nib + ib) * nkb;
-  const float* s3 = Pp.s3 + (eo * nib + ib) * nkb;
-  const int tok = token_of(a.row_token, row0 + min(r, nrows - 1), a.T);
-  const uint8_t* bq = a.xq + (size_t)tok * a.d;
-  const float* bs = a.xs + (size_t)tok * nkb;
-
-  v8i ra1[P], ra3[P], rb[P];
-  float rx[P];
-#pragma unroll
-  for (int u = 0; u < P; ++u) {
-    if (u < nkb) {
-      ra1[u] = load_frag_e4m3(a1 + u * BLK, g);
-      ra3[u] = load_frag_e4m3(a3 + u * BLK, g);
-      rb[u] = load_frag_e4m3(bq + u * BLK, g);
-      rx[u] = bs[u];
-    }
-  }
-  v4f acc1 = {0.f, 0.f, 0.f, 0.f}, acc3 = {0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = 0; kb0 < nkb; kb0 += P) {
-#pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int kb = kb0 + u;
-      if (kb < nkb) {
-        const Frag A1 = decode_e4m3(ra1[u]);
-        const Frag A3 = decode_e4m3(ra3[u]);
-        const Frag B = decode_e4m3(rb[u]);
-        const float f1 = s1[kb] * rx[u], f3 = s3[kb] * rx[u];
-        const int kn = kb + P;
-        if (kn < nkb) {
-          ra1[u] = load_frag_e4m3(a1 + kn * BLK, g);
-          ra3[u] = load_frag_e4m3(a3 + kn * BLK, g);
-          rb[u] = load_frag_e4m3(bq + kn * BLK, g);
-          rx[u] = bs[kn];
-        }
-        const v4f p1 = block_dot(A1, B);
-        const v4f p3 = block_dot(A3, B);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc1[j] = fmaf(p1[j], f1, acc1[j]);
-          acc3[j] = fmaf(p3[j], f3, acc3[j]);
-        }
-      }
-    }
-  }
-
-  __shared__ float red[8][16];
-  float hv[4];
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float gv = round_bf16(acc1[j]);
-    const float uv = round_bf16(acc3[j]);
-    const float h = round_bf16(gv / (1.f + expf(-gv)) * uv);
-    hv[j] = h;
-    amax = fmaxf(amax, fabsf(h));
-  }
-  amax = fmaxf(amax, __shfl_xor(amax, 16));
-  amax = fmaxf(amax, __shfl_xor(amax, 32));
-  if (g == 0) red[wave][r] = amax;
-  __syncthreads();
-  if (r < nrows) {
-    float m = 0.f;
-#pragma unroll
-    for (int w = 0; w < 8; ++w) m = fmaxf(m, red[w][r]);
-    const float sc = m == 0.f ? 1.f : m / E4M3_MAX;
-    const size_t row = (size_t)(row0 + r);
-    *(uint32_t*)(a.hq + row * a.I + ib * BLK + 16 * wave + 4 * g) =
-        pack4_e4m3(hv[0] / sc, hv[1] / sc, hv[2] / sc, hv[3] / sc);
-    if (wave == 0 && g == 0) a.hs[row * nib + ib] = sc;
-  }
-}
-
-template <int P>
-__global__ __launch_bounds__(512) void ffn_down_stream_kernel(FfnArgs a) {
-  const int nob = a.d / BLK, nkb = a.I / BLK;
-  const int tile = blockIdx.x / nob, ob = blockIdx.x - tile * nob;
-  if (tile >= *a.n_tiles) return;
-  const int4 td = a.tiles[tile];
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const bool sh = e >= a.E;
-  const ExpertPtrs& Pp = sh ? a.shared : a.routed;
-  const size_t eo = sh ? 0 : (size_t)e;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int o = ob * BLK + 16 * wave + r;
-  const uint8_t* aw = Pp.w2 + (eo * a.d + o) * (size_t)a.I;
-  const float* s2 = Pp.s2 + (eo * nob + ob) * nkb;
-  const size_t brow = (size_t)(row0 + min(r, nrows - 1));
-  const uint8_t* bq = a.hq + brow * a.I;
-  const float* bs = a.hs + brow * nkb;
-
-  v8i ra[P], rb[P];
-  float rx[P];
-#pragma unroll
-  for (int u = 0; u < P; ++u) {
-    if (u < nkb) {
-      ra[u] = load_frag_e4m3(aw + u * BLK, g);
-      rb[u] = load_frag_e4m3(bq + u * BLK, g);
-      rx[u] = bs[u];
-    }
-  }
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
-  for (int kb0 = 0; kb0 < nkb; kb0 += P) {
-#pragma unroll
-    for (int u = 0; u < P; ++u) {
-      const int kb = kb0 + u;
-      if (kb < nkb) {
-        const Frag A = decode_e4m3(ra[u]);
-        const Frag B = decode_e4m3(rb[u]);
-        const float f = s2[kb] * rx[u];
-        const int kn = kb + P;
-        if (kn < nkb) {
-          ra[u] = load_frag_e4m3(aw + kn * BLK, g);
-          rb[u] = load_frag_e4m3(bq + kn * BLK, g);
-          rx[u] = bs[kn];
-        }
-        const v4f p = block_dot(A, B);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] = fmaf(p[j], f, acc[j]);
-      }
-    }
-  }
-  if (r < nrows) {
-    const size_t row = (size_t)(row0 + r);
-    uint2 v;
-    v.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-    v.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-    *(uint2*)(a.out + row * a.d + ob * BLK + 16 * wave + 4 * g) = v;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// LDS-tiled variants for large batches.  A workgroup (8 waves) owns one tile
-// of up to 128 rows and 256 weight rows in two groups of 128:
+// LDS-tiled kernels.  A workgroup (8 waves) owns one tile of up to 128 rows
+// and 256 weight rows in two groups of 128:
 //   up-projection:   group 0 = w1 rows of one 128-wide h block, group 1 = the
 //                    w3 rows of the same block (so g and u of an h column meet
 //                    in the same lane and the epilogue fuses SwiGLU + h quant);
@@ -251,6 +92,12 @@ __global__ __launch_bounds__(512) void ffn_down_stream_kernel(FfnArgs a) {
 // bank-conflict free.  Wave (wr, wc) multiplies rows [64 wr, 64 wr + 64) by
 // weight rows {32 wc .. 32 wc + 31} of both groups: 4 x 4 block products per
 // K block.
+// The weight copies of a tile that is the only one of its expert (every tile
+// when T <= 128) carry the non-temporal hint: those bytes are read exactly
+// once, and full-line DMA streams with the hint reach a markedly higher HBM
+// read rate on gfx950 (about 7.0 against 6.2 TB/s in a plain read test).
+// Weights that other tiles read again are loaded with the default policy so
+// that the L2 can serve the repeat reads.
 // ---------------------------------------------------------------------------
 
 constexpr int TT_ROWS = 128;                 // activation rows per tile
@@ -262,6 +109,7 @@ constexpr int TT_STAGE = TT_A_BYTES + TT_B_BYTES + TT_S_BYTES;
 constexpr int TT_NSTAGE = 3;
 constexpr int TT_SMEM = TT_NSTAGE * TT_STAGE;
 constexpr int TT_MAX_KB = 256;               // K blocks per projection the tiled kernels support
+constexpr int CPOL_NT = 2;                   // cache-policy bits of a non-temporal load (gfx94x/gfx950)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -289,11 +137,13 @@ struct TileSrc {
   const float* s;       // scale row of activation row 64w + lane (waves 0, 1)
 };
 
+template <int WPOL>
 __device__ __forceinline__ void tile_issue(const TileSrc& src, uint8_t* stage, int kb, int wave) {
   const int off = kb * BLK;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.a[i] + off), (lds_ptr_t)(stage + (wave * 4 + i) * 1024), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.a[i] + off), (lds_ptr_t)(stage + (wave * 4 + i) * 1024), 16, 0,
+                                     WPOL);
 #pragma unroll
   for (int j = 0; j < 2; ++j)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[j] + off),
@@ -336,8 +186,9 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
 
 // Main loop shared by both projections.  src: this lane's DMA sources.
 // sa[gi][kb]: weight block scale of group gi.  acc[gi][jt][m].  mvalid
-// (wave-uniform): 16-row sub-tiles of this wave that hold rows.
-template <bool FULL>
+// (wave-uniform): 16-row sub-tiles of this wave that hold rows.  WPOL: cache
+// policy of the weight copies.
+template <bool FULL, int WPOL>
 __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const TileSrc& src, const float* const* sa,
                                                int nkb, int mvalid, v4f (&acc)[2][2][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
@@ -348,8 +199,8 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
     const int gi = i / TT_MAX_KB, kb = i - gi * TT_MAX_KB;
     if (kb < nkb) lsa[i] = sa[gi][kb];
   }
-  tile_issue(src, smem, 0, wave);
-  if (nkb > 1) tile_issue(src, smem + TT_STAGE, 1, wave);
+  tile_issue<WPOL>(src, smem, 0, wave);
+  if (nkb > 1) tile_issue<WPOL>(src, smem + TT_STAGE, 1, wave);
   tile_wait_all_but_newest(wave, nkb > 1);
   __syncthreads();
 
@@ -358,7 +209,7 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
     const bool ahead = kb + 2 < nkb;
     if (ahead) {
       const int nb = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
-      tile_issue(src, smem + nb * TT_STAGE, kb + 2, wave);
+      tile_issue<WPOL>(src, smem + nb * TT_STAGE, kb + 2, wave);
     }
     const uint8_t* la = smem + cur * TT_STAGE;
     const uint8_t* lb = la + TT_A_BYTES;
@@ -410,6 +261,23 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
     if (kb + 1 < nkb) tile_wait_all_but_newest(wave, ahead);
     pipeline_barrier();
     cur = cur == 2 ? 0 : cur + 1;
+  }
+}
+
+// The main loop for this tile: branch-free when every 16-row sub-tile of the
+// wave holds rows, non-temporal weight copies when the tile reads them once.
+__device__ __forceinline__ void run_mainloop(uint8_t* smem, float* lsa, const TileSrc& src, const float* const* sa,
+                                             int nkb, int mvalid, bool once, v4f (&acc)[2][2][4]) {
+  if (mvalid == 4) {
+    if (once)
+      tiled_mainloop<true, CPOL_NT>(smem, lsa, src, sa, nkb, mvalid, acc);
+    else
+      tiled_mainloop<true, 0>(smem, lsa, src, sa, nkb, mvalid, acc);
+  } else {
+    if (once)
+      tiled_mainloop<false, CPOL_NT>(smem, lsa, src, sa, nkb, mvalid, acc);
+    else
+      tiled_mainloop<false, 0>(smem, lsa, src, sa, nkb, mvalid, acc);
   }
 }
 
@@ -474,10 +342,7 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (mvalid == 4)
-    tiled_mainloop<true>(smem, lsa, src, sa, nkb, mvalid, acc);
-  else
-    tiled_mainloop<false>(smem, lsa, src, sa, nkb, mvalid, acc);
+  run_mainloop(smem, lsa, src, sa, nkb, mvalid, td.w != 0, acc);
 
   // epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32 columns x 64
   // rows; per-row amax over the block's 128 columns (4 waves) via LDS
@@ -553,10 +418,7 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  if (mvalid == 4)
-    tiled_mainloop<true>(smem, lsa, src, sa, nkb, mvalid, acc);
-  else
-    tiled_mainloop<false>(smem, lsa, src, sa, nkb, mvalid, acc);
+  run_mainloop(smem, lsa, src, sa, nkb, mvalid, td.w != 0, acc);
 
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -580,22 +442,15 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
   }
 }
 
-hipError_t launch_gemms(const FfnArgs& a, int tile_rows, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
-  const bool stream = tile_rows == 16;
+hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
   const int64_t g1 = max_tiles * (a.I / BLK);
-  const int64_t g2 = max_tiles * (stream ? a.d / BLK : (a.d / BLK + 1) / 2);
+  const int64_t g2 = max_tiles * ((a.d / BLK + 1) / 2);
   if (ev) (void)hipEventRecord(ev[0], s);
-  if (stream)
-    hipLaunchKernelGGL(ffn_up_stream_kernel<STREAM_DEPTH>, dim3((unsigned)g1), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(ffn_up_tiled_kernel, dim3((unsigned)g1), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(ffn_up_tiled_kernel, dim3((unsigned)g1), dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev) (void)hipEventRecord(ev[1], s);
-  if (stream)
-    hipLaunchKernelGGL(ffn_down_stream_kernel<STREAM_DEPTH>, dim3((unsigned)g2), dim3(512), 0, s, a);
-  else
-    hipLaunchKernelGGL(ffn_down_tiled_kernel, dim3((unsigned)g2), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(ffn_down_tiled_kernel, dim3((unsigned)g2), dim3(512), 0, s, a);
   err = hipGetLastError();
   if (ev) (void)hipEventRecord(ev[2], s);
   return err;
@@ -603,12 +458,7 @@ hipError_t launch_gemms(const FfnArgs& a, int tile_rows, int64_t max_tiles, hipS
 
 }  // namespace
 
-int ffn_tile_rows(int64_t T) {
-  // small batches: 16-row tiles on the streaming kernels (experts then hold a
-  // few rows each and the weights dominate the traffic)
-  if (T <= STREAM_MAX_TOKENS) return 16;
-  return 128;
-}
+int ffn_tile_rows(int64_t) { return TT_ROWS; }
 
 int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows) {
   return (T * K) / tile_rows + E + (T + tile_rows - 1) / tile_rows + 1;
@@ -641,7 +491,7 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
   a.hq = hq;
   a.hs = hs;
   a.out = out;
-  return launch_gemms(a, NT, max_tiles, s, ev);
+  return launch_gemms(a, max_tiles, s, ev);
 }
 
 }  // namespace moe
