@@ -137,30 +137,42 @@ struct TileSrc {
   const float* s;       // scale row of activation row 64w + lane (waves 0, 1)
 };
 
+// act (wave-uniform): this wave's activation rows [16w, 16w + 16) hold tile
+// rows; otherwise no MFMA reads them and they are not copied.
 template <int WPOL>
-__device__ __forceinline__ void tile_issue(const TileSrc& src, uint8_t* stage, int kb, int wave) {
+__device__ __forceinline__ void tile_issue(const TileSrc& src, uint8_t* stage, int kb, int wave, bool act) {
   const int off = kb * BLK;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.a[i] + off), (lds_ptr_t)(stage + (wave * 4 + i) * 1024), 16, 0,
                                      WPOL);
+  if (act) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[j] + off),
-                                     (lds_ptr_t)(stage + TT_A_BYTES + (wave * 2 + j) * 1024), 16, 0, 0);
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[j] + off),
+                                       (lds_ptr_t)(stage + TT_A_BYTES + (wave * 2 + j) * 1024), 16, 0, 0);
+  }
   if (wave < 2)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.s + kb), (lds_ptr_t)(stage + TT_A_BYTES + TT_B_BYTES + wave * 256),
                                      4, 0, 0);
 }
 
-// wait until this wave's copies of every stage but the newest one have landed
-__device__ __forceinline__ void tile_wait_all_but_newest(int wave, bool newest_issued) {
+// Wait until this wave's copies of every stage but the newest one have
+// landed: the newest stage's copies are the 4 weight pieces, 2 activation
+// pieces when `act`, and one scale copy on waves 0 and 1.
+__device__ __forceinline__ void tile_wait_all_but_newest(int wave, bool newest_issued, bool act) {
   if (!newest_issued) {
     wait_vmcnt<0>();
   } else if (wave < 2) {
-    wait_vmcnt<7>();
+    if (act)
+      wait_vmcnt<7>();
+    else
+      wait_vmcnt<5>();
   } else {
-    wait_vmcnt<6>();
+    if (act)
+      wait_vmcnt<6>();
+    else
+      wait_vmcnt<4>();
   }
 }
 
@@ -190,7 +202,7 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
 // policy of the weight copies.
 template <bool FULL, int WPOL>
 __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const TileSrc& src, const float* const* sa,
-                                               int nkb, int mvalid, v4f (&acc)[2][2][4]) {
+                                               int nkb, int nrows, int mvalid, v4f (&acc)[2][2][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
 
@@ -199,9 +211,10 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
     const int gi = i / TT_MAX_KB, kb = i - gi * TT_MAX_KB;
     if (kb < nkb) lsa[i] = sa[gi][kb];
   }
-  tile_issue<WPOL>(src, smem, 0, wave);
-  if (nkb > 1) tile_issue<WPOL>(src, smem + TT_STAGE, 1, wave);
-  tile_wait_all_but_newest(wave, nkb > 1);
+  const bool act = 16 * wave < nrows;
+  tile_issue<WPOL>(src, smem, 0, wave, act);
+  if (nkb > 1) tile_issue<WPOL>(src, smem + TT_STAGE, 1, wave, act);
+  tile_wait_all_but_newest(wave, nkb > 1, act);
   __syncthreads();
 
   int cur = 0;  // stage buffer holding K block kb
@@ -209,7 +222,7 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
     const bool ahead = kb + 2 < nkb;
     if (ahead) {
       const int nb = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
-      tile_issue<WPOL>(src, smem + nb * TT_STAGE, kb + 2, wave);
+      tile_issue<WPOL>(src, smem + nb * TT_STAGE, kb + 2, wave, act);
     }
     const uint8_t* la = smem + cur * TT_STAGE;
     const uint8_t* lb = la + TT_A_BYTES;
@@ -258,7 +271,7 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
         }
       }
     }
-    if (kb + 1 < nkb) tile_wait_all_but_newest(wave, ahead);
+    if (kb + 1 < nkb) tile_wait_all_but_newest(wave, ahead, act);
     pipeline_barrier();
     cur = cur == 2 ? 0 : cur + 1;
   }
@@ -267,17 +280,17 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
 // The main loop for this tile: branch-free when every 16-row sub-tile of the
 // wave holds rows, non-temporal weight copies when the tile reads them once.
 __device__ __forceinline__ void run_mainloop(uint8_t* smem, float* lsa, const TileSrc& src, const float* const* sa,
-                                             int nkb, int mvalid, bool once, v4f (&acc)[2][2][4]) {
+                                             int nkb, int nrows, int mvalid, bool once, v4f (&acc)[2][2][4]) {
   if (mvalid == 4) {
     if (once)
-      tiled_mainloop<true, CPOL_NT>(smem, lsa, src, sa, nkb, mvalid, acc);
+      tiled_mainloop<true, CPOL_NT>(smem, lsa, src, sa, nkb, nrows, mvalid, acc);
     else
-      tiled_mainloop<true, 0>(smem, lsa, src, sa, nkb, mvalid, acc);
+      tiled_mainloop<true, 0>(smem, lsa, src, sa, nkb, nrows, mvalid, acc);
   } else {
     if (once)
-      tiled_mainloop<false, CPOL_NT>(smem, lsa, src, sa, nkb, mvalid, acc);
+      tiled_mainloop<false, CPOL_NT>(smem, lsa, src, sa, nkb, nrows, mvalid, acc);
     else
-      tiled_mainloop<false, 0>(smem, lsa, src, sa, nkb, mvalid, acc);
+      tiled_mainloop<false, 0>(smem, lsa, src, sa, nkb, nrows, mvalid, acc);
   }
 }
 
@@ -342,7 +355,7 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop(smem, lsa, src, sa, nkb, mvalid, td.w != 0, acc);
+  run_mainloop(smem, lsa, src, sa, nkb, nrows, mvalid, td.w != 0, acc);
 
   // epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32 columns x 64
   // rows; per-row amax over the block's 128 columns (4 waves) via LDS
@@ -418,7 +431,7 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop(smem, lsa, src, sa, nkb, mvalid, td.w != 0, acc);
+  run_mainloop(smem, lsa, src, sa, nkb, nrows, mvalid, td.w != 0, acc);
 
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
