@@ -113,6 +113,10 @@ constexpr int CPOL_NT = 2;                   // cache-policy bits of a non-tempo
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+// Read-only data addressed uniformly by the workgroup (the weight block
+// scales): loads through the constant address space become scalar loads,
+// which are counted apart from the vector-memory copies the pipeline waits on.
+typedef const __attribute__((address_space(4))) float* const_f32_ptr;
 
 // LDS holds each 128-byte row unpadded with its 16-byte chunks permuted:
 // chunk c of row r sits at slot c ^ swz(r).  Sixteen consecutive rows then
@@ -197,25 +201,21 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
 }
 
 // Main loop shared by both projections.  src: this lane's DMA sources.
-// sa[gi][kb]: weight block scale of group gi.  acc[gi][jt][m].  mvalid
-// (wave-uniform): 16-row sub-tiles of this wave that hold rows.  WPOL: cache
-// policy of the weight copies.
+// sa0, sa1: weight block scales of the two weight groups over K.
+// acc[gi][jt][m].  mvalid (wave-uniform): 16-row sub-tiles of this wave that
+// hold rows.  WPOL: cache policy of the weight copies.
 template <bool FULL, int WPOL>
-__device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const TileSrc& src, const float* const* sa,
-                                               int nkb, int nrows, int mvalid, v4f (&acc)[2][2][4]) {
+__device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src, const_f32_ptr sa0,
+                                               const_f32_ptr sa1, int nkb, int nrows, int mvalid,
+                                               v4f (&acc)[2][2][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
 
-  // the weight block scales of the whole K range, read once (published by the first barrier)
-  for (int i = threadIdx.x; i < 2 * TT_MAX_KB; i += blockDim.x) {
-    const int gi = i / TT_MAX_KB, kb = i - gi * TT_MAX_KB;
-    if (kb < nkb) lsa[i] = sa[gi][kb];
-  }
   const bool act = 16 * wave < nrows;
   tile_issue<WPOL>(src, smem, 0, wave, act);
   if (nkb > 1) tile_issue<WPOL>(src, smem + TT_STAGE, 1, wave, act);
   tile_wait_all_but_newest(wave, nkb > 1, act);
-  __syncthreads();
+  pipeline_barrier();
 
   int cur = 0;  // stage buffer holding K block kb
   for (int kb = 0; kb < nkb; ++kb) {
@@ -227,45 +227,48 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
     const uint8_t* la = smem + cur * TT_STAGE;
     const uint8_t* lb = la + TT_A_BYTES;
     const float* ls = (const float*)(lb + TT_B_BYTES);
-    const float s_a0 = lsa[kb], s_a1 = lsa[TT_MAX_KB + kb];
-    Frag B[4];
-    float sb[4];
+    const float s_a0 = sa0[kb], s_a1 = sa1[kb];
+    // a wave whose 64 rows hold no tile row only helps with the copies
+    if (FULL || mvalid > 0) {
+      Frag B[4];
+      float sb[4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      if (FULL || m < mvalid) {
-        B[m] = decode_e4m3(lds_frag(lb, wr * 64 + 16 * m + r, g));
-        sb[m] = ls[wr * 64 + 16 * m + r];
+      for (int m = 0; m < 4; ++m) {
+        if (FULL || m < mvalid) {
+          B[m] = decode_e4m3(lds_frag(lb, wr * 64 + 16 * m + r, g));
+          sb[m] = ls[wr * 64 + 16 * m + r];
+        }
       }
-    }
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
+      for (int gi = 0; gi < 2; ++gi) {
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const Frag A = decode_e4m3(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
-        const float sg = gi == 0 ? s_a0 : s_a1;
-        if constexpr (FULL) {
-          // four independent accumulation chains, issued round-robin
-          v4f p[4];
+        for (int jt = 0; jt < 2; ++jt) {
+          const Frag A = decode_e4m3(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
+          const float sg = gi == 0 ? s_a0 : s_a1;
+          if constexpr (FULL) {
+            // four independent accumulation chains, issued round-robin
+            v4f p[4];
 #pragma unroll
-          for (int m = 0; m < 4; ++m) p[m] = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int m = 0; m < 4; ++m) p[m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+            for (int q = 0; q < 4; ++q)
 #pragma unroll
-            for (int m = 0; m < 4; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], p[m], 0, 0, 0);
+              for (int m = 0; m < 4; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], p[m], 0, 0, 0);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const float f = sg * sb[m];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[m][j], f, acc[gi][jt][m][j]);
-          }
-        } else {
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            if (m < mvalid) {
-              const v4f p = block_dot(A, B[m]);
+            for (int m = 0; m < 4; ++m) {
               const float f = sg * sb[m];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[j], f, acc[gi][jt][m][j]);
+              for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[m][j], f, acc[gi][jt][m][j]);
+            }
+          } else {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              if (m < mvalid) {
+                const v4f p = block_dot(A, B[m]);
+                const float f = sg * sb[m];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[j], f, acc[gi][jt][m][j]);
+              }
             }
           }
         }
@@ -279,18 +282,19 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, float* lsa, const 
 
 // The main loop for this tile: branch-free when every 16-row sub-tile of the
 // wave holds rows, non-temporal weight copies when the tile reads them once.
-__device__ __forceinline__ void run_mainloop(uint8_t* smem, float* lsa, const TileSrc& src, const float* const* sa,
+__device__ __forceinline__ void run_mainloop(uint8_t* smem, const TileSrc& src, const float* sa0, const float* sa1,
                                              int nkb, int nrows, int mvalid, bool once, v4f (&acc)[2][2][4]) {
+  const const_f32_ptr c0 = (const_f32_ptr)sa0, c1 = (const_f32_ptr)sa1;
   if (mvalid == 4) {
     if (once)
-      tiled_mainloop<true, CPOL_NT>(smem, lsa, src, sa, nkb, nrows, mvalid, acc);
+      tiled_mainloop<true, CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
     else
-      tiled_mainloop<true, 0>(smem, lsa, src, sa, nkb, nrows, mvalid, acc);
+      tiled_mainloop<true, 0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
   } else {
     if (once)
-      tiled_mainloop<false, CPOL_NT>(smem, lsa, src, sa, nkb, nrows, mvalid, acc);
+      tiled_mainloop<false, CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
     else
-      tiled_mainloop<false, 0>(smem, lsa, src, sa, nkb, nrows, mvalid, acc);
+      tiled_mainloop<false, 0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
   }
 }
 
@@ -319,7 +323,6 @@ __device__ __forceinline__ TileSrc make_tile_src(WRow wrow, ARow arow, SRow srow
 // grid = max_tiles * (I/128), block = 512
 __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[TT_SMEM];
-  __shared__ float lsa[2 * TT_MAX_KB];
   const int nib = a.I / BLK, nkb = a.d / BLK;
   const int tile = blockIdx.x / nib, ib = blockIdx.x - tile * nib;
   if (tile >= *a.n_tiles) return;  // uniform for the whole block, before any barrier
@@ -355,7 +358,7 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop(smem, lsa, src, sa, nkb, nrows, mvalid, td.w != 0, acc);
+  run_mainloop(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
 
   // epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32 columns x 64
   // rows; per-row amax over the block's 128 columns (4 waves) via LDS
@@ -400,7 +403,6 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
 // grid = max_tiles * ceil(d/256), block = 512
 __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[TT_SMEM];
-  __shared__ float lsa[2 * TT_MAX_KB];
   const int nob = a.d / BLK, nkb = a.I / BLK;
   const int nob2 = (nob + 1) >> 1;
   const int tile = blockIdx.x / nob2, ob = blockIdx.x - tile * nob2;
@@ -431,7 +433,7 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop(smem, lsa, src, sa, nkb, nrows, mvalid, td.w != 0, acc);
+  run_mainloop(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
 
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
