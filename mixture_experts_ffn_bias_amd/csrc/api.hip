@@ -12,7 +12,7 @@ using namespace moe;
 namespace {
 
 constexpr size_t WS_ALIGN = 256;
-constexpr int MAX_FEATURES = 32768;  // 256 K blocks per projection in the tiled FFN kernels
+constexpr int MAX_FEATURES = 32768;  // keeps every row offset and grid size well inside int32
 
 struct Layout {
   size_t zpart, idx, w, chunk_cnt, chunk_off, counts, offsets, row_token, pair_row, tiles, n_tiles, xq, xs, hq,

@@ -108,7 +108,6 @@ constexpr int TT_S_BYTES = TT_ROWS * 4;      // activation scales of one K block
 constexpr int TT_STAGE = TT_A_BYTES + TT_B_BYTES + TT_S_BYTES;
 constexpr int TT_NSTAGE = 3;
 constexpr int TT_SMEM = TT_NSTAGE * TT_STAGE;
-constexpr int TT_MAX_KB = 256;               // K blocks per projection the tiled kernels support
 constexpr int CPOL_NT = 2;                   // cache-policy bits of a non-temporal load (gfx94x/gfx950)
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -202,12 +201,13 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
 
 // Main loop shared by both projections.  src: this lane's DMA sources.
 // sa0, sa1: weight block scales of the two weight groups over K.
-// acc[gi][jt][m].  mvalid (wave-uniform): 16-row sub-tiles of this wave that
-// hold rows.  WPOL: cache policy of the weight copies.
-template <bool FULL, int WPOL>
+// acc[gi][jt][m].  MV: the 16-row sub-tiles of this wave that hold rows
+// (0..4; a compile-time count keeps the K-block body free of branches, so the
+// LDS reads, decodes and MFMAs of a block can be interleaved).  WPOL: cache
+// policy of the weight copies.
+template <int MV, int WPOL>
 __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src, const_f32_ptr sa0,
-                                               const_f32_ptr sa1, int nkb, int nrows, int mvalid,
-                                               v4f (&acc)[2][2][4]) {
+                                               const_f32_ptr sa1, int nkb, int nrows, v4f (&acc)[2][2][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
 
@@ -224,20 +224,18 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src
       const int nb = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
       tile_issue<WPOL>(src, smem + nb * TT_STAGE, kb + 2, wave, act);
     }
-    const uint8_t* la = smem + cur * TT_STAGE;
-    const uint8_t* lb = la + TT_A_BYTES;
-    const float* ls = (const float*)(lb + TT_B_BYTES);
-    const float s_a0 = sa0[kb], s_a1 = sa1[kb];
-    // a wave whose 64 rows hold no tile row only helps with the copies
-    if (FULL || mvalid > 0) {
-      Frag B[4];
-      float sb[4];
+    // a wave whose 64 rows hold no tile row (MV = 0) only helps with the copies
+    if constexpr (MV > 0) {
+      const uint8_t* la = smem + cur * TT_STAGE;
+      const uint8_t* lb = la + TT_A_BYTES;
+      const float* ls = (const float*)(lb + TT_B_BYTES);
+      const float s_a0 = sa0[kb], s_a1 = sa1[kb];
+      Frag B[MV];
+      float sb[MV];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        if (FULL || m < mvalid) {
-          B[m] = decode_e4m3(lds_frag(lb, wr * 64 + 16 * m + r, g));
-          sb[m] = ls[wr * 64 + 16 * m + r];
-        }
+      for (int m = 0; m < MV; ++m) {
+        B[m] = decode_e4m3(lds_frag(lb, wr * 64 + 16 * m + r, g));
+        sb[m] = ls[wr * 64 + 16 * m + r];
       }
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
@@ -245,31 +243,19 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src
         for (int jt = 0; jt < 2; ++jt) {
           const Frag A = decode_e4m3(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
           const float sg = gi == 0 ? s_a0 : s_a1;
-          if constexpr (FULL) {
-            // four independent accumulation chains, issued round-robin
-            v4f p[4];
+          // MV independent accumulation chains, issued round-robin
+          v4f p[MV];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) p[m] = v4f{0.f, 0.f, 0.f, 0.f};
+          for (int m = 0; m < MV; ++m) p[m] = v4f{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
+          for (int q = 0; q < 4; ++q)
 #pragma unroll
-              for (int m = 0; m < 4; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], p[m], 0, 0, 0);
+            for (int m = 0; m < MV; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], p[m], 0, 0, 0);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              const float f = sg * sb[m];
+          for (int m = 0; m < MV; ++m) {
+            const float f = sg * sb[m];
 #pragma unroll
-              for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[m][j], f, acc[gi][jt][m][j]);
-            }
-          } else {
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              if (m < mvalid) {
-                const v4f p = block_dot(A, B[m]);
-                const float f = sg * sb[m];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[j], f, acc[gi][jt][m][j]);
-              }
-            }
+            for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[m][j], f, acc[gi][jt][m][j]);
           }
         }
       }
@@ -280,22 +266,28 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src
   }
 }
 
-// The main loop for this tile: branch-free when every 16-row sub-tile of the
-// wave holds rows, non-temporal weight copies when the tile reads them once.
+template <int WPOL>
+__device__ __forceinline__ void run_mainloop_pol(uint8_t* smem, const TileSrc& src, const_f32_ptr c0, const_f32_ptr c1,
+                                                 int nkb, int nrows, int mvalid, v4f (&acc)[2][2][4]) {
+  switch (mvalid) {
+    case 0: tiled_mainloop<0, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    case 1: tiled_mainloop<1, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    case 2: tiled_mainloop<2, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    case 3: tiled_mainloop<3, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    default: tiled_mainloop<4, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+  }
+}
+
+// The main loop for this tile (mvalid: wave-uniform count of this wave's
+// 16-row sub-tiles that hold rows), with non-temporal weight copies when the
+// tile reads them once.
 __device__ __forceinline__ void run_mainloop(uint8_t* smem, const TileSrc& src, const float* sa0, const float* sa1,
                                              int nkb, int nrows, int mvalid, bool once, v4f (&acc)[2][2][4]) {
   const const_f32_ptr c0 = (const_f32_ptr)sa0, c1 = (const_f32_ptr)sa1;
-  if (mvalid == 4) {
-    if (once)
-      tiled_mainloop<true, CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
-    else
-      tiled_mainloop<true, 0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
-  } else {
-    if (once)
-      tiled_mainloop<false, CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
-    else
-      tiled_mainloop<false, 0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
-  }
+  if (once)
+    run_mainloop_pol<CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
+  else
+    run_mainloop_pol<0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
 }
 
 // DMA source pointers of this lane.  wrow(i): weight row of tile row i
