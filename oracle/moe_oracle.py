@@ -18,7 +18,7 @@ What it computes, and where each step comes from (page titles as printed):
 * "DeepSeek-V3.2-Exp · Gate projection", expert excerpt: an expert is
   ``w2((silu(w1(x).float()) * w3(x).float()).type_as(x))``; Linear excerpt:
   weights are [out, in], FP8 weights carry one float32 scale per 128x128
-  block (``block_size = 128``), no bias.
+  block (``block_size = 128``), wider (bf16) weights carry none, no bias.
 * "DeepSeek-V3.2-Exp · MoE update", rmsnorm excerpt: with a residual, the
   residual is added in float32, the sum (cast back) becomes the new residual,
   and the normalised sum is ``weight * x * rsqrt(mean(x^2) + eps)``, eps 1e-6.
@@ -63,7 +63,8 @@ __all__ = [
     "BLOCK", "E4M3_MAX", "RMS_EPS",
     "e4m3_table", "e4m3_decode", "e4m3_encode", "bf16_round", "bf16_bits_to_f64",
     "f64_to_bf16_bits", "dequant_weight", "quant_act", "dequant_act", "gate", "permute",
-    "silu", "expert_ffn", "moe_forward", "add_rmsnorm", "param_count", "weights_for",
+    "silu", "expert_ffn", "expert_ffn_bf16", "bf16_weight", "moe_forward", "add_rmsnorm", "param_count",
+    "weights_for",
 ]
 
 
@@ -286,12 +287,53 @@ def expert_ffn(x_rows, w1, s1, w3, s3, w2, s2, full: bool = False):
     return o
 
 
+def expert_ffn_bf16(x_rows, w1, w3, w2, full: bool = False):
+    """The same expert with bf16 weights: w2((silu(w1 x) * w3 x)) without scales.
+
+    "Gate projection", Linear excerpt: a weight whose elements are wider
+    than one byte gets no scale parameter.  The Linear forward is not on the
+    pages; read plainly, it multiplies the bf16 activation by the bf16
+    weight [out, in] (no activation quantisation) and returns bf16:
+    g = bf16(x . W1^T), u = bf16(x . W3^T), h = bf16(silu(g) * u),
+    o = bf16(h . W2^T), each dot product exact in float64 before its rounding.
+    """
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    W1 = np.asarray(w1, dtype=np.float64)
+    W3 = np.asarray(w3, dtype=np.float64)
+    W2 = np.asarray(w2, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        g = bf16_round(x_rows @ W1.T)
+        u = bf16_round(x_rows @ W3.T)
+        h = bf16_round(silu(g) * u)
+        o = bf16_round(h @ W2.T)
+    if full:
+        return {"o": o, "g": g, "u": u, "h": h}
+    return o
+
+
 def _expert(params, e: Optional[int]):
     if e is None:  # the shared expert
         names = ("sh_w1", "sh_s1", "sh_w3", "sh_s3", "sh_w2", "sh_s2")
         return [np.asarray(params[n][0]) for n in names]
     names = ("w1", "s1", "w3", "s3", "w2", "s2")
     return [np.asarray(params[n][e]) for n in names]
+
+
+def _run_expert(params, e: Optional[int], x_rows):
+    """Expert e (None: the shared one) on x_rows, FP8 or bf16 by the weights it holds."""
+    if "s1" not in params:  # bf16 weights: no scales
+        pre, i = ("sh_", 0) if e is None else ("", e)
+        return expert_ffn_bf16(x_rows, bf16_weight(params[pre + "w1"][i]), bf16_weight(params[pre + "w3"][i]),
+                               bf16_weight(params[pre + "w2"][i]))
+    return expert_ffn(x_rows, *_expert(params, e))
+
+
+def bf16_weight(w) -> np.ndarray:
+    """A bf16 weight given as raw bit patterns (uint16 / int16) or as values -> float64."""
+    a = np.asarray(w)
+    if a.dtype in (np.uint16, np.int16):
+        return bf16_bits_to_f64(a.view(np.uint16))
+    return a.astype(np.float64)
 
 
 # --------------------------------------------------------------------------
@@ -304,7 +346,8 @@ def moe_forward(x, params, dims, tokens: Optional[Sequence[int]] = None,
     """Forward of one MoE layer on bf16 x [T, d] (given as float64 values).
 
     params: mapping with gate_w [E, d], gate_b [E] and per-expert indexable
-    w1/s1/w3/s3/w2/s2 (routed, [E, ...]) and sh_w1/... (shared, [1, ...]).
+    w1/s1/w3/s3/w2/s2 (routed, [E, ...]) and sh_w1/... (shared, [1, ...]);
+    without s1/s3/s2 the expert weights are bf16 (expert_ffn_bf16).
     tokens: evaluate the expert part only for these tokens (routing is always
     computed for all).  idx: force this selection [T, K] (weights then come
     from the oracle's own scores).  routing: a gate() result to reuse.
@@ -325,9 +368,9 @@ def moe_forward(x, params, dims, tokens: Optional[Sequence[int]] = None,
         rows, ks = np.nonzero(ti == e)             # ascending token
         if rows.size == 0:
             continue
-        o = expert_ffn(x[tok[rows]], *_expert(params, e))
+        o = _run_expert(params, e, x[tok[rows]])
         y[rows] += o * tw[rows, ks][:, None]
-    y += expert_ffn(x[tok], *_expert(params, None))  # shared expert, every token
+    y += _run_expert(params, None, x[tok])  # shared expert, every token
     return {"idx": sel_idx, "w": w_all, "routing": r, "tokens": tok, "y": y, "delta": bf16_round(y)}
 
 

@@ -118,6 +118,23 @@ def expert_weights(dims: Dims, n: int, device, seed: int, tag0: int) -> Dict[str
     return out
 
 
+def expert_weights_bf16(dims: Dims, n: int, device, seed: int, tag0: int) -> Dict[str, torch.Tensor]:
+    """n SwiGLU experts with bf16 weights (no scales): w1, w3 [n, inter, d]; w2 [n, d, inter].
+
+    Same normal laws (and seeds) as expert_weights, rounded to bf16 instead of block-quantised.
+    """
+    d, I = dims.d_model, dims.inter
+    out = {
+        "w1": torch.empty((n, I, d), dtype=torch.bfloat16, device=device),
+        "w3": torch.empty((n, I, d), dtype=torch.bfloat16, device=device),
+        "w2": torch.empty((n, d, I), dtype=torch.bfloat16, device=device),
+    }
+    for e in range(n):
+        for j, (wn, shape, fan_in) in enumerate((("w1", (I, d), d), ("w3", (I, d), d), ("w2", (d, I), I))):
+            out[wn][e].copy_(_normal(shape, math.sqrt(1.0 / fan_in), device, seed, tag0 + 3 * e + j))
+    return out
+
+
 def gate_bias(dims: Dims, law: str, device, seed: int, tag: int) -> torch.Tensor:
     E = dims.n_experts
     if law == "zero":
@@ -132,15 +149,20 @@ def gate_bias(dims: Dims, law: str, device, seed: int, tag: int) -> torch.Tensor
     raise ValueError(law)
 
 
-def make_block(dims: Dims, bias_law: str, device, seed: int, block: int = 0) -> Dict[str, torch.Tensor]:
-    """Parameters of one MoE layer: router weight/bias, 256 routed + 1 shared expert."""
+def make_block(dims: Dims, bias_law: str, device, seed: int, block: int = 0,
+               weights: str = "e4m3") -> Dict[str, torch.Tensor]:
+    """Parameters of one MoE layer: router weight/bias, routed + 1 shared expert.
+
+    weights: "e4m3" (block-quantised with scales) or "bf16" (no scales).
+    """
     t = 1000 + block * 100_000
     p = {
         "gate_w": _normal((dims.n_experts, dims.d_model), math.sqrt(1.0 / dims.d_model), device, seed, t + 1),
         "gate_b": gate_bias(dims, bias_law, device, seed, t + 2),
     }
-    routed = expert_weights(dims, dims.n_experts, device, seed, t + 10)
-    shared = expert_weights(dims, 1, device, seed, t + 10 + 3 * dims.n_experts + 5)
+    make = {"e4m3": expert_weights, "bf16": expert_weights_bf16}[weights]
+    routed = make(dims, dims.n_experts, device, seed, t + 10)
+    shared = make(dims, 1, device, seed, t + 10 + 3 * dims.n_experts + 5)
     p.update({k: v for k, v in routed.items()})
     p.update({"sh_" + k: v for k, v in shared.items()})
     return p
