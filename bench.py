@@ -1,6 +1,7 @@
 """Benchmark of the DeepSeek-V3.2-Exp MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|stack4|tiny]
+                    [--weights e4m3|bf16]
 
 A step is one pass of the whole layer (router, permutation, grouped expert
 FFN, combine; for the stacked workload four blocks of fused residual-add
@@ -100,24 +101,38 @@ def measured_traffic(workload: str, kernel: str):
     return int((e["fetch_kib"] * t["fetch_factor"] + e["write_kib"] * t["write_factor"]) * 1024)
 
 
-def algorithmic_work(dims, T, touched):
+def algorithmic_work(dims, T, touched, bf16=False):
     """Bytes and FLOPs each kernel must move / compute (implementation buffers excluded).
 
     touched: number of routed experts with at least one row (the shared expert comes on top).
+    bf16: bf16 expert weights without scales, bf16 activations (x read, h written and read).
     """
     d, I, K = dims.d_model, dims.inter, dims.topk
     R = T * K + T                                  # routed rows + shared rows
     ne = touched + 1
-    up_w = 2 * I * d + 2 * (I // 128) * (d // 128) * 4
-    dn_w = I * d + (d // 128) * (I // 128) * 4
-    up_bytes = ne * up_w + T * d + T * (d // 128) * 4 + R * (I + (I // 128) * 4)
-    dn_bytes = ne * dn_w + R * (I + (I // 128) * 4) + R * d * 2
+    if bf16:
+        up_w, dn_w = 2 * (2 * I * d), 2 * I * d
+        x_bytes, h_bytes = T * d * 2, R * I * 2
+    else:
+        up_w = 2 * I * d + 2 * (I // 128) * (d // 128) * 4
+        dn_w = I * d + (d // 128) * (I // 128) * 4
+        x_bytes, h_bytes = T * d + T * (d // 128) * 4, R * (I + (I // 128) * 4)
+    up_bytes = ne * up_w + x_bytes + h_bytes
+    dn_bytes = ne * dn_w + h_bytes + R * d * 2
     return {
         "ffn_up": {"bytes": up_bytes, "flops": 2 * R * d * 2 * I},
         "ffn_down": {"bytes": dn_bytes, "flops": 2 * R * I * d},
         "layer_bytes": ne * (up_w + dn_w) + dims.n_experts * d * 4 + dims.n_experts * 4 + 2 * T * d * 2,
         "layer_flops": 2 * R * 3 * d * I,
     }
+
+
+def _host(t):
+    """Host numpy copy; bf16 comes back as its uint16 bit patterns (the oracle's bf16 weight form)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu()
+    return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
 
 def cpu_baseline(x, params, dims, budget_s, threads, residual=None, gain=None, seed=0):
@@ -139,13 +154,13 @@ def cpu_baseline(x, params, dims, budget_s, threads, residual=None, gain=None, s
     rng = np.random.default_rng(seed)
     T = x.shape[0]
     order = rng.permutation(T)
-    names = ("w1", "s1", "w3", "s3", "w2", "s2")
+    names = ("w1", "s1", "w3", "s3", "w2", "s2") if "s1" in params else ("w1", "w3", "w2")
     xv_all = x.float().cpu().numpy().astype(np.float64)
     rv_all = residual.float().cpu().numpy().astype(np.float64) if residual is not None else None
     gv = gain.cpu().numpy() if gain is not None else None
     host = {"gate_w": params["gate_w"].cpu().numpy(), "gate_b": params["gate_b"].cpu().numpy()}
     for n in names:
-        host["sh_" + n] = params["sh_" + n].cpu().numpy()
+        host["sh_" + n] = _host(params["sh_" + n])
     cache = {}
 
     class Rows:
@@ -154,7 +169,7 @@ def cpu_baseline(x, params, dims, budget_s, threads, residual=None, gain=None, s
 
         def __getitem__(self, e):
             if (self.n, e) not in cache:           # only reached if a batch needs an unfetched expert
-                cache[(self.n, e)] = params[self.n][e].cpu().numpy()
+                cache[(self.n, e)] = _host(params[self.n][e])
             return cache[(self.n, e)]
 
     for n in names:
@@ -193,6 +208,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skewed", "stack4"])
+    ap.add_argument("--weights", default="e4m3", choices=["e4m3", "bf16"],
+                    help="expert weights: FP8 e4m3 with 128x128 block scales (the layer's), or bf16 without scales")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -223,7 +240,8 @@ def main():
         return
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
-    data = synth.make_workload(args.workload, device=dev)
+    bf16 = args.weights == "bf16"
+    data = synth.make_workload(args.workload, device=dev, weights=args.weights)
     T = data["tokens"]
     cd = moe.make_dims(dims.d_model, dims.n_experts, dims.n_groups, dims.topk_groups, dims.topk, dims.inter,
                        dims.route_scale)
@@ -243,12 +261,15 @@ def main():
     hev = HipEvents()
     torch.cuda.synchronize()
 
+    fwd = moe.moe_forward_bf16 if bf16 else moe.moe_forward
+    fwd_timed = moe.moe_forward_bf16_timed if bf16 else moe.moe_forward_timed
+
     def step(events=None):
         if nb == 1:
             if events is None:
-                moe.moe_forward(cd, layers[0].weights, T, x0, delta, idx[0], w[0], ws, stream)
+                fwd(cd, layers[0].weights, T, x0, delta, idx[0], w[0], ws, stream)
             else:
-                moe.moe_forward_timed(cd, layers[0].weights, T, x0, delta, idx[0], w[0], ws, events[0], stream)
+                fwd_timed(cd, layers[0].weights, T, x0, delta, idx[0], w[0], ws, events[0], stream)
             return
         res.copy_(res0)
         src = x0
@@ -256,9 +277,9 @@ def main():
             moe.moe_add_rmsnorm(dims.d_model, T, src, res, data["gains"][b], 1e-6, h, stream)
             out = delta if b == nb - 1 else cur
             if events is None:
-                moe.moe_forward(cd, layers[b].weights, T, h, out, idx[b], w[b], ws, stream)
+                fwd(cd, layers[b].weights, T, h, out, idx[b], w[b], ws, stream)
             else:
-                moe.moe_forward_timed(cd, layers[b].weights, T, h, out, idx[b], w[b], ws, events[b], stream)
+                fwd_timed(cd, layers[b].weights, T, h, out, idx[b], w[b], ws, events[b], stream)
             src = out
 
     for _ in range(args.warmup):
@@ -287,7 +308,7 @@ def main():
     # algorithmic work of the dominant kernel (per launch; blocks of the stack are alike)
     counts = [np.bincount(i.cpu().numpy().ravel(), minlength=dims.n_experts) for i in idx]
     touched = [int((c > 0).sum()) for c in counts]
-    work = [algorithmic_work(dims, T, t) for t in touched]
+    work = [algorithmic_work(dims, T, t, bf16) for t in touched]
     dom = max(("ffn_up", "ffn_down"), key=lambda s: stage_avg[s])
     dur = stage_avg[dom] * 1e-3
     bytes_per = sum(wk[dom]["bytes"] for wk in work) / nb
@@ -300,7 +321,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4)}
-    roof.update({"kernel": dom, "traffic": measured_traffic(args.workload, dom), "launch_ms": round(stage_avg[dom], 4),
+    traffic_key = args.workload + ("_bf16" if bf16 else "")
+    roof.update({"kernel": dom, "traffic": measured_traffic(traffic_key, dom), "launch_ms": round(stage_avg[dom], 4),
                  "alg_bytes": int(bytes_per), "alg_flops": int(flops_per)})
 
     tokens = T * K
@@ -321,7 +343,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": T, "blocks": nb, "d_model": dims.d_model,
                    "experts": dims.n_experts, "groups": dims.n_groups, "topk_groups": dims.topk_groups,
-                   "topk": dims.topk, "inter": dims.inter, "weights": "e4m3 + fp32 128x128 block scales",
+                   "topk": dims.topk, "inter": dims.inter,
+                   "weights": "bf16, no scales" if bf16 else "e4m3 + fp32 128x128 block scales",
                    "touched_experts": touched},
         "roofline": roof,
         "layer": {"alg_bytes_per_step": int(layer_bytes), "hbm_GBps": round(layer_bytes / step_s / 1e9, 1),

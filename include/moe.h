@@ -81,6 +81,25 @@ typedef struct {
   moe_experts shared;  /* n = 1, applied to every token ("Add shared output") */
 } moe_weights;
 
+/* n SwiGLU experts with bf16 Linear layers.  A Linear whose weight elements
+ * are wider than one byte carries no scale ("Gate projection", Linear
+ * excerpt: the constructor registers no scale parameter then); such a Linear
+ * multiplies the bf16 activation itself, without quantisation.
+ * Layout as moe_experts, elements bf16 (uint16_t bit patterns). */
+typedef struct {
+  const uint16_t* w1; /* bf16 [n][inter][d]    (16-byte aligned) */
+  const uint16_t* w3; /* bf16 [n][inter][d]    (16-byte aligned) */
+  const uint16_t* w2; /* bf16 [n][d][inter]    (16-byte aligned) */
+} moe_experts_bf16;
+
+/* All parameters of one MoE layer with bf16 expert weights. */
+typedef struct {
+  const float* gate_w;     /* fp32 [E][d] router weight */
+  const float* gate_b;     /* fp32 [E]    router bias */
+  moe_experts_bf16 routed; /* n = E */
+  moe_experts_bf16 shared; /* n = 1 */
+} moe_weights_bf16;
+
 /* Workspace bytes that any single entry point below (including moe_forward)
  * needs for `tokens` tokens.  Returns 0 for invalid dims. */
 size_t moe_workspace_size(const moe_dims* dims, int64_t tokens);
@@ -112,7 +131,8 @@ int moe_gate(const moe_dims* dims, int64_t tokens, const uint16_t* x, const floa
  *   pair_row   int32 [T][K]      out: row of (token t, choice k)
  *   xq         e4m3  [T][d]      out: per-128-block quantised x (16-byte aligned)
  *   xs         fp32  [T][d/128]  out: block scales, amax/448 (1 for an all-zero block)
- * Needs the workspace. */
+ * xq and xs may both be NULL: the quantisation is then skipped (bf16-weight
+ * experts take x itself).  Needs the workspace. */
 int moe_permute(const moe_dims* dims, int64_t tokens, const int32_t* idx, const uint16_t* x,
                 int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* pair_row,
                 uint8_t* xq, float* xs, void* workspace, size_t workspace_bytes, void* stream);
@@ -132,6 +152,20 @@ int moe_grouped_ffn(const moe_dims* dims, int64_t tokens, const moe_experts* rou
                     const moe_experts* shared, const int32_t* offsets, const int32_t* row_token,
                     const uint8_t* xq, const float* xs, uint16_t* out, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* moe_grouped_ffn for bf16-weight experts: the same SwiGLU with bf16 Linear
+ * layers and no quantisation,
+ *   g = bf16(x . W1_e^T), u = bf16(x . W3_e^T), h = bf16(silu(g) * u), out[r] = bf16(h . W2_e^T)
+ * (fp32 accumulation; bf16 MFMAs on the operands as given).
+ *   routed, shared  bf16 expert weights (shared may be NULL: shared rows are then skipped)
+ *   offsets, row_token   from moe_permute (which may skip its quantisation)
+ *   x               bf16 [T][d] the layer input (16-byte aligned)
+ *   out             bf16 [T*K + T][d] out, one row per permuted row (16-byte aligned)
+ * Needs the workspace. */
+int moe_grouped_ffn_bf16(const moe_dims* dims, int64_t tokens, const moe_experts_bf16* routed,
+                         const moe_experts_bf16* shared, const int32_t* offsets, const int32_t* row_token,
+                         const uint16_t* x, uint16_t* out, void* workspace, size_t workspace_bytes,
+                         void* stream);
 
 /* Router-weighted combine plus shared output ("MoE update": ``y[idx] +=
  * expert(x[idx]) * weights[idx, top]`` in ascending expert order, then
@@ -164,6 +198,18 @@ int moe_forward_timed(const moe_dims* dims, const moe_weights* weights, int64_t 
                       const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
                       void* workspace, size_t workspace_bytes, void* stream,
                       void* const* stage_events);
+
+/* moe_forward with bf16 expert weights (moe_grouped_ffn_bf16 in place of the
+ * quantised FFN; the router is the same). */
+int moe_forward_bf16(const moe_dims* dims, const moe_weights_bf16* weights, int64_t tokens,
+                     const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
+                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_forward_bf16 recording the stage events of moe_forward_timed. */
+int moe_forward_bf16_timed(const moe_dims* dims, const moe_weights_bf16* weights, int64_t tokens,
+                           const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
+                           void* workspace, size_t workspace_bytes, void* stream,
+                           void* const* stage_events);
 
 /* Fused residual add + RMSNorm ("MoE update", rmsnorm excerpt, residual branch):
  *   r = float(x) + float(residual);  residual <- bf16(r);

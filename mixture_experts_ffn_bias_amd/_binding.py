@@ -17,8 +17,9 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK = 0
-SYMBOLS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward",
-           "moe_forward_timed", "moe_add_rmsnorm", "moe_mlp_workspace_size", "moe_mlp", "moe_status_string")
+SYMBOLS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_bf16", "moe_combine",
+           "moe_forward", "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_add_rmsnorm",
+           "moe_mlp_workspace_size", "moe_mlp", "moe_status_string")
 MOE_FORWARD_EVENTS = 6
 
 
@@ -43,6 +44,15 @@ class moe_weights(ctypes.Structure):
                 ("shared", moe_experts)]
 
 
+class moe_experts_bf16(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("w1", "w3", "w2")]
+
+
+class moe_weights_bf16(ctypes.Structure):
+    _fields_ = [("gate_w", ctypes.c_void_p), ("gate_b", ctypes.c_void_p), ("routed", moe_experts_bf16),
+                ("shared", moe_experts_bf16)]
+
+
 _lib = None
 
 
@@ -61,16 +71,21 @@ def lib() -> ctypes.CDLL:
         L.moe_permute.argtypes = [dp, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_grouped_ffn.argtypes = [dp, i64, ctypes.POINTER(moe_experts), ctypes.POINTER(moe_experts), vp, vp, vp,
                                       vp, vp, vp, sz, vp]
+        L.moe_grouped_ffn_bf16.argtypes = [dp, i64, ctypes.POINTER(moe_experts_bf16), ctypes.POINTER(moe_experts_bf16),
+                                           vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.argtypes = [dp, i64, vp, vp, vp, vp, i32, vp, vp]
         L.moe_forward.argtypes = [dp, ctypes.POINTER(moe_weights), i64, vp, vp, vp, vp, vp, sz, vp]
         L.moe_forward_timed.argtypes = [dp, ctypes.POINTER(moe_weights), i64, vp, vp, vp, vp, vp, sz, vp,
                                         ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_forward_bf16.argtypes = [dp, ctypes.POINTER(moe_weights_bf16), i64, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_forward_bf16_timed.argtypes = [dp, ctypes.POINTER(moe_weights_bf16), i64, vp, vp, vp, vp, vp, sz, vp,
+                                             ctypes.POINTER(ctypes.c_void_p)]
         L.moe_add_rmsnorm.argtypes = [i32, i64, vp, vp, vp, ctypes.c_float, vp, vp]
         L.moe_mlp_workspace_size.argtypes = [i32, i32, i64]
         L.moe_mlp_workspace_size.restype = sz
         L.moe_mlp.argtypes = [i32, i32, i64, ctypes.POINTER(moe_experts), vp, vp, vp, sz, vp]
-        for n in ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_forward", "moe_forward_timed",
-                  "moe_add_rmsnorm", "moe_mlp"):
+        for n in ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_bf16", "moe_combine", "moe_forward",
+                  "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_add_rmsnorm", "moe_mlp"):
             getattr(L, n).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -141,6 +156,18 @@ def moe_grouped_ffn(dims, tokens, routed: moe_experts, shared: Optional[moe_expe
                                  _stream(stream)), "moe_grouped_ffn")
 
 
+def experts_struct_bf16(w1, w3, w2) -> moe_experts_bf16:
+    return moe_experts_bf16(_p(w1), _p(w3), _p(w2))
+
+
+def moe_grouped_ffn_bf16(dims, tokens, routed: moe_experts_bf16, shared: Optional[moe_experts_bf16], offsets,
+                         row_token, x, out, ws, stream=None):
+    _check(lib().moe_grouped_ffn_bf16(ctypes.byref(dims), int(tokens), ctypes.byref(routed),
+                                      ctypes.byref(shared) if shared is not None else None, _p(offsets),
+                                      _p(row_token), _p(x), _p(out), _p(ws), ws.numel() if ws is not None else 0,
+                                      _stream(stream)), "moe_grouped_ffn_bf16")
+
+
 def moe_combine(dims, tokens, idx, w, pair_row, rows, has_shared, delta, stream=None):
     _check(lib().moe_combine(ctypes.byref(dims), int(tokens), _p(idx), _p(w), _p(pair_row), _p(rows),
                              1 if has_shared else 0, _p(delta), _stream(stream)), "moe_combine")
@@ -158,6 +185,20 @@ def moe_forward_timed(dims, weights: moe_weights, tokens, x, delta, idx_out, w_o
     _check(lib().moe_forward_timed(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta),
                                    _p(idx_out), _p(w_out), _p(ws), ws.numel() if ws is not None else 0,
                                    _stream(stream), arr), "moe_forward_timed")
+
+
+def moe_forward_bf16(dims, weights: moe_weights_bf16, tokens, x, delta, idx_out, w_out, ws, stream=None):
+    _check(lib().moe_forward_bf16(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta),
+                                  _p(idx_out), _p(w_out), _p(ws), ws.numel() if ws is not None else 0,
+                                  _stream(stream)), "moe_forward_bf16")
+
+
+def moe_forward_bf16_timed(dims, weights: moe_weights_bf16, tokens, x, delta, idx_out, w_out, ws, events,
+                           stream=None):
+    arr = (ctypes.c_void_p * MOE_FORWARD_EVENTS)(*events)
+    _check(lib().moe_forward_bf16_timed(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta),
+                                        _p(idx_out), _p(w_out), _p(ws), ws.numel() if ws is not None else 0,
+                                        _stream(stream), arr), "moe_forward_bf16_timed")
 
 
 def moe_add_rmsnorm(d, tokens, x, residual, gain, eps, out, stream=None):
@@ -190,29 +231,39 @@ class MoELayer:
     params: gate_w fp32 [E, d], gate_b fp32 [E], w1/w3 uint8 [E, I, d],
     w2 uint8 [E, d, I], s1/s3 fp32 [E, I/128, d/128], s2 fp32 [E, d/128, I/128],
     and the same with an ``sh_`` prefix for the shared expert (leading dim 1).
+    With bf16 w1/w3/w2 (and no scales) the layer runs moe_forward_bf16.
     """
 
     def __init__(self, dims: moe_dims, params: Dict[str, torch.Tensor]):
         self.dims = dims
         E, d, I = dims.n_experts, dims.d_model, dims.inter
+        self.bf16 = params["w1"].dtype == torch.bfloat16
+        wdt = torch.bfloat16 if self.bf16 else torch.uint8
         want = {"gate_w": ((E, d), torch.float32), "gate_b": ((E,), torch.float32)}
         for pre, n in (("", E), ("sh_", 1)):
-            want[pre + "w1"] = ((n, I, d), torch.uint8)
-            want[pre + "w3"] = ((n, I, d), torch.uint8)
-            want[pre + "w2"] = ((n, d, I), torch.uint8)
-            want[pre + "s1"] = ((n, I // 128, d // 128), torch.float32)
-            want[pre + "s3"] = ((n, I // 128, d // 128), torch.float32)
-            want[pre + "s2"] = ((n, d // 128, I // 128), torch.float32)
+            want[pre + "w1"] = ((n, I, d), wdt)
+            want[pre + "w3"] = ((n, I, d), wdt)
+            want[pre + "w2"] = ((n, d, I), wdt)
+            if not self.bf16:
+                want[pre + "s1"] = ((n, I // 128, d // 128), torch.float32)
+                want[pre + "s3"] = ((n, I // 128, d // 128), torch.float32)
+                want[pre + "s2"] = ((n, d // 128, I // 128), torch.float32)
         for k, (shape, dt) in want.items():
             t = params[k]
             if tuple(t.shape) != shape or t.dtype != dt or not t.is_contiguous() or t.device.type != "cuda":
                 raise ValueError(f"{k}: expected contiguous {dt} {shape} on the GPU, got {t.dtype} "
                                  f"{tuple(t.shape)} on {t.device}")
         self.params = params
-        self.weights = moe_weights(
-            _p(params["gate_w"]), _p(params["gate_b"]),
-            experts_struct(*(params[k] for k in _EXPERT_KEYS)),
-            experts_struct(*(params["sh_" + k] for k in _EXPERT_KEYS)))
+        if self.bf16:
+            self.weights = moe_weights_bf16(
+                _p(params["gate_w"]), _p(params["gate_b"]),
+                experts_struct_bf16(*(params[k] for k in ("w1", "w3", "w2"))),
+                experts_struct_bf16(*(params["sh_" + k] for k in ("w1", "w3", "w2"))))
+        else:
+            self.weights = moe_weights(
+                _p(params["gate_w"]), _p(params["gate_b"]),
+                experts_struct(*(params[k] for k in _EXPERT_KEYS)),
+                experts_struct(*(params["sh_" + k] for k in _EXPERT_KEYS)))
         self._ws: Optional[torch.Tensor] = None
 
     def workspace(self, tokens: int) -> torch.Tensor:
@@ -227,7 +278,8 @@ class MoELayer:
         T = x.shape[0]
         if delta is None:
             delta = torch.empty_like(x)
-        moe_forward(self.dims, self.weights, T, x, delta, idx, w, self.workspace(T), stream)
+        run = moe_forward_bf16 if self.bf16 else moe_forward
+        run(self.dims, self.weights, T, x, delta, idx, w, self.workspace(T), stream)
         return delta
 
     __call__ = forward

@@ -46,7 +46,7 @@ Layout layout(const moe_dims& dm, int64_t T) {
   L.n_tiles = take(4);
   L.xq = take(t * d);
   L.xs = take(t * (d / BLK) * 4);
-  L.hq = take(rows * I);
+  L.hq = take(rows * I * 2);  // e4m3 h, or bf16 h with bf16 expert weights
   L.hs = take(rows * (I / BLK) * 4);
   L.rows = take(rows * d * 2);
   L.total = off;
@@ -118,6 +118,16 @@ int check_experts(const moe_experts* x) {
 
 ExpertPtrs ptrs(const moe_experts& x) { return ExpertPtrs{x.w1, x.w3, x.w2, x.s1, x.s3, x.s2}; }
 
+int check_experts_bf16(const moe_experts_bf16* x) {
+  if (!x || !x->w1 || !x->w3 || !x->w2) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x->w1, 16) || !aligned(x->w3, 16) || !aligned(x->w2, 16)) return MOE_ERR_ALIGN;
+  return MOE_OK;
+}
+
+ExpertPtrs ptrs(const moe_experts_bf16& x) {
+  return ExpertPtrs{(const uint8_t*)x.w1, (const uint8_t*)x.w3, (const uint8_t*)x.w2, nullptr, nullptr, nullptr};
+}
+
 template <typename T>
 T* at(void* ws, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
@@ -163,7 +173,7 @@ int moe_permute(const moe_dims* dims, int64_t tokens, const int32_t* idx, const 
   MOE_TRY(check_dims(dims));
   MOE_TRY(check_tokens(*dims, tokens));
   if (tokens == 0) return MOE_OK;
-  if (!idx || !x || !counts || !offsets || !row_token || !pair_row || !xq || !xs) return MOE_ERR_INVALID_ARG;
+  if (!idx || !x || !counts || !offsets || !row_token || !pair_row || (!xq) != (!xs)) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(xq, 16) || !aligned(idx, 4) || !aligned(counts, 4) || !aligned(offsets, 4) ||
       !aligned(row_token, 4) || !aligned(pair_row, 4) || !aligned(xs, 4))
     return MOE_ERR_ALIGN;
@@ -200,6 +210,29 @@ int moe_grouped_ffn(const moe_dims* dims, int64_t tokens, const moe_experts* rou
                                at<float>(workspace, L.hs), out, (hipStream_t)stream));
 }
 
+int moe_grouped_ffn_bf16(const moe_dims* dims, int64_t tokens, const moe_experts_bf16* routed,
+                         const moe_experts_bf16* shared, const int32_t* offsets, const int32_t* row_token,
+                         const uint16_t* x, uint16_t* out, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  MOE_TRY(check_experts_bf16(routed));
+  if (shared) MOE_TRY(check_experts_bf16(shared));
+  if (!offsets || !row_token || !x || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(offsets, 4) || !aligned(row_token, 4)) return MOE_ERR_ALIGN;
+  const Layout L = layout(*dims, tokens);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
+  const moe_dims& d = *dims;
+  const ExpertPtrs rp = ptrs(*routed);
+  ExpertPtrs sp;
+  if (shared) sp = ptrs(*shared);
+  return hip_status(launch_ffn(rp, shared ? &sp : nullptr, (int)tokens, d.d_model, d.inter, d.n_experts, d.topk,
+                               offsets, row_token, (const uint8_t*)x, nullptr, at<int4>(workspace, L.tiles),
+                               at<int32_t>(workspace, L.n_tiles), at<uint8_t>(workspace, L.hq), nullptr, out,
+                               (hipStream_t)stream, nullptr, true));
+}
+
 int moe_combine(const moe_dims* dims, int64_t tokens, const int32_t* idx, const float* w, const int32_t* pair_row,
                 const uint16_t* rows, int32_t has_shared, uint16_t* delta, void* stream) {
   MOE_TRY(check_dims(dims));
@@ -219,17 +252,14 @@ namespace {
 
 // The fused forward.  ev: NULL or MOE_FORWARD_EVENTS events, recorded before
 // the gate, before the permutation, before the up-projection, before the
-// down-projection, before the combine and after it.
-int forward_impl(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
-                 uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
-                 hipStream_t s, hipEvent_t* ev) {
-  MOE_TRY(check_dims(dims));
-  MOE_TRY(check_tokens(*dims, tokens));
-  if (tokens == 0) return MOE_OK;
-  if (!weights || !weights->gate_w || !weights->gate_b || !x || !delta) return MOE_ERR_INVALID_ARG;
-  MOE_TRY(check_experts(&weights->routed));
-  MOE_TRY(check_experts(&weights->shared));
-  if (!aligned(x, 16) || !aligned(delta, 16) || !aligned(weights->gate_w, 16) || !aligned(weights->gate_b, 4) ||
+// down-projection, before the combine and after it.  routed / shared: the
+// expert weights, e4m3 with scales or (bf16 = true) bf16 without.
+int forward_impl(const moe_dims* dims, const float* gate_w, const float* gate_b, const ExpertPtrs& routed,
+                 const ExpertPtrs& shared, bool bf16, int64_t tokens, const uint16_t* x, uint16_t* delta,
+                 int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes, hipStream_t s,
+                 hipEvent_t* ev) {
+  if (!gate_w || !gate_b || !x || !delta) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(delta, 16) || !aligned(gate_w, 16) || !aligned(gate_b, 4) ||
       (idx_out && !aligned(idx_out, 4)) || (w_out && !aligned(w_out, 4)))
     return MOE_ERR_ALIGN;
   const Layout L = layout(*dims, tokens);
@@ -242,25 +272,60 @@ int forward_impl(const moe_dims* dims, const moe_weights* weights, int64_t token
   int32_t* offsets = at<int32_t>(workspace, L.offsets);
   int32_t* row_token = at<int32_t>(workspace, L.row_token);
   int32_t* pair_row = at<int32_t>(workspace, L.pair_row);
-  uint8_t* xq = at<uint8_t>(workspace, L.xq);
-  float* xs = at<float>(workspace, L.xs);
+  // e4m3 weights take the quantised x; bf16 weights take x itself
+  uint8_t* xq = bf16 ? nullptr : at<uint8_t>(workspace, L.xq);
+  float* xs = bf16 ? nullptr : at<float>(workspace, L.xs);
   uint16_t* rows = at<uint16_t>(workspace, L.rows);
   if (ev) (void)hipEventRecord(ev[0], s);
-  MOE_TRY(hip_status(launch_gate(x, weights->gate_w, weights->gate_b, T, d.d_model, d.n_experts, d.n_groups,
-                                 d.topk_groups, d.topk, d.route_scale, at<float>(workspace, L.zpart),
+  MOE_TRY(hip_status(launch_gate(x, gate_w, gate_b, T, d.d_model, d.n_experts, d.n_groups, d.topk_groups, d.topk,
+                                 d.route_scale, at<float>(workspace, L.zpart),
                                  gate_ksplit(tokens, d.d_model, d.n_experts), idx, w, s)));
   if (ev) (void)hipEventRecord(ev[1], s);
   MOE_TRY(hip_status(launch_permute(idx, x, T, d.d_model, d.n_experts, d.topk, at<int32_t>(workspace, L.chunk_cnt),
                                     at<int32_t>(workspace, L.chunk_off), at<int32_t>(workspace, L.counts), offsets,
                                     row_token, pair_row, xq, xs, s)));
-  const ExpertPtrs rp = ptrs(weights->routed), sp = ptrs(weights->shared);
-  MOE_TRY(hip_status(launch_ffn(rp, &sp, T, d.d_model, d.inter, d.n_experts, d.topk, offsets, row_token, xq, xs,
-                                at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
-                                at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), rows, s,
-                                ev ? ev + 2 : nullptr)));
+  MOE_TRY(hip_status(launch_ffn(routed, &shared, T, d.d_model, d.inter, d.n_experts, d.topk, offsets, row_token,
+                                bf16 ? (const uint8_t*)x : xq, xs, at<int4>(workspace, L.tiles),
+                                at<int32_t>(workspace, L.n_tiles), at<uint8_t>(workspace, L.hq),
+                                bf16 ? nullptr : at<float>(workspace, L.hs), rows, s, ev ? ev + 2 : nullptr, bf16)));
   const int st = hip_status(launch_combine(idx, w, pair_row, rows, 1, T, d.topk, d.n_experts, d.d_model, delta, s));
   if (ev) (void)hipEventRecord(ev[5], s);
   return st;
+}
+
+int forward_bf16(const moe_dims* dims, const moe_weights_bf16* weights, int64_t tokens, const uint16_t* x,
+                 uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                 hipStream_t s, hipEvent_t* ev) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  if (!weights) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_experts_bf16(&weights->routed));
+  MOE_TRY(check_experts_bf16(&weights->shared));
+  return forward_impl(dims, weights->gate_w, weights->gate_b, ptrs(weights->routed), ptrs(weights->shared), true,
+                      tokens, x, delta, idx_out, w_out, workspace, workspace_bytes, s, ev);
+}
+
+int take_events(void* const* stage_events, hipEvent_t* ev) {
+  if (!stage_events) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < MOE_FORWARD_EVENTS; ++i) {
+    if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
+    ev[i] = (hipEvent_t)stage_events[i];
+  }
+  return MOE_OK;
+}
+
+int forward_fp8(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
+                uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                hipStream_t s, hipEvent_t* ev) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  if (!weights) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_experts(&weights->routed));
+  MOE_TRY(check_experts(&weights->shared));
+  return forward_impl(dims, weights->gate_w, weights->gate_b, ptrs(weights->routed), ptrs(weights->shared), false,
+                      tokens, x, delta, idx_out, w_out, workspace, workspace_bytes, s, ev);
 }
 
 }  // namespace
@@ -270,20 +335,32 @@ extern "C" {
 int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
                 uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
                 void* stream) {
-  return forward_impl(dims, weights, tokens, x, delta, idx_out, w_out, workspace, workspace_bytes,
-                      (hipStream_t)stream, nullptr);
+  return forward_fp8(dims, weights, tokens, x, delta, idx_out, w_out, workspace, workspace_bytes,
+                     (hipStream_t)stream, nullptr);
 }
 
 int moe_forward_timed(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
                       uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
                       void* stream, void* const* stage_events) {
-  if (!stage_events) return MOE_ERR_INVALID_ARG;
   hipEvent_t ev[MOE_FORWARD_EVENTS];
-  for (int i = 0; i < MOE_FORWARD_EVENTS; ++i) {
-    if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
-    ev[i] = (hipEvent_t)stage_events[i];
-  }
-  return forward_impl(dims, weights, tokens, x, delta, idx_out, w_out, workspace, workspace_bytes,
+  MOE_TRY(take_events(stage_events, ev));
+  return forward_fp8(dims, weights, tokens, x, delta, idx_out, w_out, workspace, workspace_bytes,
+                     (hipStream_t)stream, ev);
+}
+
+int moe_forward_bf16(const moe_dims* dims, const moe_weights_bf16* weights, int64_t tokens, const uint16_t* x,
+                     uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                     void* stream) {
+  return forward_bf16(dims, weights, tokens, x, delta, idx_out, w_out, workspace, workspace_bytes,
+                      (hipStream_t)stream, nullptr);
+}
+
+int moe_forward_bf16_timed(const moe_dims* dims, const moe_weights_bf16* weights, int64_t tokens, const uint16_t* x,
+                           uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* stage_events) {
+  hipEvent_t ev[MOE_FORWARD_EVENTS];
+  MOE_TRY(take_events(stage_events, ev));
+  return forward_bf16(dims, weights, tokens, x, delta, idx_out, w_out, workspace, workspace_bytes,
                       (hipStream_t)stream, ev);
 }
 

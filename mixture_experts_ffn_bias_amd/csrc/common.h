@@ -69,6 +69,19 @@ __device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float 
   return (uint32_t)v;
 }
 
+// 32 bytes of bf16 (16 values: the lane's share of one 64-deep K block) as
+// the operands of two 16x16x32 bf16 MFMAs.
+struct FragH {
+  v8bf k[2];
+};
+
+__device__ __forceinline__ FragH as_bf16(v8i q) {
+  FragH f;
+  f.k[0] = __builtin_bit_cast(v8bf, v4i{q[0], q[1], q[2], q[3]});
+  f.k[1] = __builtin_bit_cast(v8bf, v4i{q[4], q[5], q[6], q[7]});
+  return f;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

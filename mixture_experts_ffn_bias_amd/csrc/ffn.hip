@@ -63,6 +63,9 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
   if (threadIdx.x == 0) *n_tiles = nsh + min(s[255], cap);
 }
 
+// With e4m3 weights, xq/hq are e4m3 rows with block scales xs/hs; with bf16
+// weights (no scales), xq is the bf16 input x, hq receives bf16 h and the
+// scale pointers are unused.
 struct FfnArgs {
   ExpertPtrs routed;
   ExpertPtrs shared;
@@ -142,7 +145,7 @@ struct TileSrc {
 
 // act (wave-uniform): this wave's activation rows [16w, 16w + 16) hold tile
 // rows; otherwise no MFMA reads them and they are not copied.
-template <int WPOL>
+template <bool BF, int WPOL>
 __device__ __forceinline__ void tile_issue(const TileSrc& src, uint8_t* stage, int kb, int wave, bool act) {
   const int off = kb * BLK;
 #pragma unroll
@@ -155,18 +158,19 @@ __device__ __forceinline__ void tile_issue(const TileSrc& src, uint8_t* stage, i
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[j] + off),
                                        (lds_ptr_t)(stage + TT_A_BYTES + (wave * 2 + j) * 1024), 16, 0, 0);
   }
-  if (wave < 2)
+  if (!BF && wave < 2)
     __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.s + kb), (lds_ptr_t)(stage + TT_A_BYTES + TT_B_BYTES + wave * 256),
                                      4, 0, 0);
 }
 
 // Wait until this wave's copies of every stage but the newest one have
 // landed: the newest stage's copies are the 4 weight pieces, 2 activation
-// pieces when `act`, and one scale copy on waves 0 and 1.
+// pieces when `act`, and (e4m3 only) one scale copy on waves 0 and 1.
+template <bool BF>
 __device__ __forceinline__ void tile_wait_all_but_newest(int wave, bool newest_issued, bool act) {
   if (!newest_issued) {
     wait_vmcnt<0>();
-  } else if (wave < 2) {
+  } else if (!BF && wave < 2) {
     if (act)
       wait_vmcnt<7>();
     else
@@ -205,16 +209,16 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
 // (0..4; a compile-time count keeps the K-block body free of branches, so the
 // LDS reads, decodes and MFMAs of a block can be interleaved).  WPOL: cache
 // policy of the weight copies.
-template <int MV, int WPOL>
+template <bool BF, int MV, int WPOL>
 __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src, const_f32_ptr sa0,
                                                const_f32_ptr sa1, int nkb, int nrows, v4f (&acc)[2][2][4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
 
   const bool act = 16 * wave < nrows;
-  tile_issue<WPOL>(src, smem, 0, wave, act);
-  if (nkb > 1) tile_issue<WPOL>(src, smem + TT_STAGE, 1, wave, act);
-  tile_wait_all_but_newest(wave, nkb > 1, act);
+  tile_issue<BF, WPOL>(src, smem, 0, wave, act);
+  if (nkb > 1) tile_issue<BF, WPOL>(src, smem + TT_STAGE, 1, wave, act);
+  tile_wait_all_but_newest<BF>(wave, nkb > 1, act);
   pipeline_barrier();
 
   int cur = 0;  // stage buffer holding K block kb
@@ -222,10 +226,30 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src
     const bool ahead = kb + 2 < nkb;
     if (ahead) {
       const int nb = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
-      tile_issue<WPOL>(src, smem + nb * TT_STAGE, kb + 2, wave, act);
+      tile_issue<BF, WPOL>(src, smem + nb * TT_STAGE, kb + 2, wave, act);
     }
     // a wave whose 64 rows hold no tile row (MV = 0) only helps with the copies
-    if constexpr (MV > 0) {
+    if constexpr (BF && MV > 0) {
+      // bf16 operands: the 128 bytes of a row are 64 k values, two MFMAs per block, no scales
+      const uint8_t* la = smem + cur * TT_STAGE;
+      const uint8_t* lb = la + TT_A_BYTES;
+      FragH B[MV];
+#pragma unroll
+      for (int m = 0; m < MV; ++m) B[m] = as_bf16(lds_frag(lb, wr * 64 + 16 * m + r, g));
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          const FragH A = as_bf16(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
+#pragma unroll
+          for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int m = 0; m < MV; ++m)
+              acc[gi][jt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], acc[gi][jt][m], 0, 0, 0);
+        }
+      }
+    }
+    if constexpr (!BF && MV > 0) {
       const uint8_t* la = smem + cur * TT_STAGE;
       const uint8_t* lb = la + TT_A_BYTES;
       const float* ls = (const float*)(lb + TT_B_BYTES);
@@ -260,34 +284,35 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src
         }
       }
     }
-    if (kb + 1 < nkb) tile_wait_all_but_newest(wave, ahead, act);
+    if (kb + 1 < nkb) tile_wait_all_but_newest<BF>(wave, ahead, act);
     pipeline_barrier();
     cur = cur == 2 ? 0 : cur + 1;
   }
 }
 
-template <int WPOL>
+template <bool BF, int WPOL>
 __device__ __forceinline__ void run_mainloop_pol(uint8_t* smem, const TileSrc& src, const_f32_ptr c0, const_f32_ptr c1,
                                                  int nkb, int nrows, int mvalid, v4f (&acc)[2][2][4]) {
   switch (mvalid) {
-    case 0: tiled_mainloop<0, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    case 1: tiled_mainloop<1, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    case 2: tiled_mainloop<2, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    case 3: tiled_mainloop<3, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    default: tiled_mainloop<4, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    case 0: tiled_mainloop<BF, 0, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    case 1: tiled_mainloop<BF, 1, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    case 2: tiled_mainloop<BF, 2, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    case 3: tiled_mainloop<BF, 3, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    default: tiled_mainloop<BF, 4, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
   }
 }
 
 // The main loop for this tile (mvalid: wave-uniform count of this wave's
 // 16-row sub-tiles that hold rows), with non-temporal weight copies when the
 // tile reads them once.
+template <bool BF>
 __device__ __forceinline__ void run_mainloop(uint8_t* smem, const TileSrc& src, const float* sa0, const float* sa1,
                                              int nkb, int nrows, int mvalid, bool once, v4f (&acc)[2][2][4]) {
   const const_f32_ptr c0 = (const_f32_ptr)sa0, c1 = (const_f32_ptr)sa1;
   if (once)
-    run_mainloop_pol<CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
+    run_mainloop_pol<BF, CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
   else
-    run_mainloop_pol<0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
+    run_mainloop_pol<BF, 0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
 }
 
 // DMA source pointers of this lane.  wrow(i): weight row of tile row i
@@ -312,10 +337,13 @@ __device__ __forceinline__ TileSrc make_tile_src(WRow wrow, ARow arow, SRow srow
   return t;
 }
 
-// grid = max_tiles * (I/128), block = 512
+// grid = max_tiles * (I/128), block = 512.  BF: bf16 weights and activations
+// (64-element K blocks, no scales, h stored as bf16).
+template <bool BF>
 __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[TT_SMEM];
-  const int nib = a.I / BLK, nkb = a.d / BLK;
+  constexpr int EB = BF ? 2 : 1;  // bytes per element
+  const int nib = a.I / BLK, nkb = a.d * EB / BLK;
   const int tile = blockIdx.x / nib, ib = blockIdx.x - tile * nib;
   if (tile >= *a.n_tiles) return;  // uniform for the whole block, before any barrier
   const int4 td = a.tiles[tile];
@@ -331,17 +359,18 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
   const TileSrc src = make_tile_src(
       [&](int row) {  // 0..127: w1 rows of block ib, 128..255: w3 rows
         const uint8_t* base = row < 128 ? P.w1 : P.w3;
-        return base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d;
+        return base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d * EB;
       },
       [&](int row) {
         const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T);
-        return a.xq + (size_t)tok * a.d;
+        return a.xq + (size_t)tok * a.d * EB;
       },
-      [&](int row) {
+      [&](int row) -> const float* {
+        if (BF) return nullptr;
         const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T);
         return a.xs + (size_t)tok * nkb;
       });
-  const float* sa[2] = {P.s1 + (eo * nib + ib) * nkb, P.s3 + (eo * nib + ib) * nkb};
+  const float* sa[2] = {BF ? nullptr : P.s1 + (eo * nib + ib) * nkb, BF ? nullptr : P.s3 + (eo * nib + ib) * nkb};
   const int mvalid = __builtin_amdgcn_readfirstlane(min(4, max(0, (nrows - wr * 64 + 15) >> 4)));
   v4f acc[2][2][4];
 #pragma unroll
@@ -350,7 +379,33 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
+  run_mainloop<BF>(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
+
+  if constexpr (BF) {
+    // h = bf16(silu(bf16 g) * bf16 u), stored as bf16
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int rr = wr * 64 + 16 * m + r;
+      if (rr < nrows) {
+        const size_t row = (size_t)(row0 + rr);
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt) {
+          uint16_t hb[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gv = round_bf16(acc[0][jt][m][j]);
+            const float uv = round_bf16(acc[1][jt][m][j]);
+            hb[j] = f32_to_bf16(gv / (1.f + expf(-gv)) * uv);
+          }
+          uint2 o;
+          o.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
+          o.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
+          *(uint2*)((uint16_t*)a.hq + row * a.I + ib * BLK + wc * 32 + jt * 16 + 4 * g) = o;
+        }
+      }
+    }
+    return;
+  }
 
   // epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32 columns x 64
   // rows; per-row amax over the block's 128 columns (4 waves) via LDS
@@ -392,10 +447,12 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
   }
 }
 
-// grid = max_tiles * ceil(d/256), block = 512
+// grid = max_tiles * ceil(d/256), block = 512.  BF: bf16 weights and h.
+template <bool BF>
 __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[TT_SMEM];
-  const int nob = a.d / BLK, nkb = a.I / BLK;
+  constexpr int EB = BF ? 2 : 1;  // bytes per element
+  const int nob = a.d / BLK, nkb = a.I * EB / BLK;
   const int nob2 = (nob + 1) >> 1;
   const int tile = blockIdx.x / nob2, ob = blockIdx.x - tile * nob2;
   if (tile >= *a.n_tiles) return;
@@ -411,12 +468,14 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
   const TileSrc src = make_tile_src(
       [&](int row) {  // a ragged last pair of blocks reads a valid row
         const int o = min(ob * 256 + row, a.d - 1);
-        return P.w2 + (eo * a.d + o) * (size_t)a.I;
+        return P.w2 + (eo * a.d + o) * (size_t)a.I * EB;
       },
-      [&](int row) { return a.hq + (size_t)(row0 + min(row, nrows - 1)) * a.I; },
-      [&](int row) { return a.hs + (size_t)(row0 + min(row, nrows - 1)) * nkb; });
-  const float* sa[2] = {P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb,
-                        P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb};
+      [&](int row) { return a.hq + (size_t)(row0 + min(row, nrows - 1)) * a.I * EB; },
+      [&](int row) -> const float* {
+        return BF ? nullptr : a.hs + (size_t)(row0 + min(row, nrows - 1)) * nkb;
+      });
+  const float* sa[2] = {BF ? nullptr : P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb,
+                        BF ? nullptr : P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb};
   const int mvalid = __builtin_amdgcn_readfirstlane(min(4, max(0, (nrows - wr * 64 + 15) >> 4)));
   v4f acc[2][2][4];
 #pragma unroll
@@ -425,7 +484,7 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
+  run_mainloop<BF>(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
 
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
@@ -449,15 +508,16 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
   }
 }
 
+template <bool BF>
 hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
   const int64_t g1 = max_tiles * (a.I / BLK);
   const int64_t g2 = max_tiles * ((a.d / BLK + 1) / 2);
   if (ev) (void)hipEventRecord(ev[0], s);
-  hipLaunchKernelGGL(ffn_up_tiled_kernel, dim3((unsigned)g1), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(ffn_up_tiled_kernel<BF>, dim3((unsigned)g1), dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev) (void)hipEventRecord(ev[1], s);
-  hipLaunchKernelGGL(ffn_down_tiled_kernel, dim3((unsigned)g2), dim3(512), 0, s, a);
+  hipLaunchKernelGGL(ffn_down_tiled_kernel<BF>, dim3((unsigned)g2), dim3(512), 0, s, a);
   err = hipGetLastError();
   if (ev) (void)hipEventRecord(ev[2], s);
   return err;
@@ -474,7 +534,7 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows) {
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E, int K,
                       const int32_t* offsets, const int32_t* row_token, const uint8_t* xq, const float* xs,
                       int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs, uint16_t* out, hipStream_t s,
-                      hipEvent_t* ev) {
+                      hipEvent_t* ev, bool bf16) {
   const int NT = ffn_tile_rows(T);
   const int64_t max_tiles = ffn_max_tiles(T, K, E, NT);
   const int nsh = shared ? (T + NT - 1) / NT : 0;
@@ -498,7 +558,7 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
   a.hq = hq;
   a.hs = hs;
   a.out = out;
-  return launch_gemms(a, max_tiles, s, ev);
+  return bf16 ? launch_gemms<true>(a, max_tiles, s, ev) : launch_gemms<false>(a, max_tiles, s, ev);
 }
 
 }  // namespace moe

@@ -39,10 +39,13 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
 // rows 0..T-1 (offsets is then not read).
 // ev: NULL, or three events recorded before the up-projection, before the
 // down-projection and after it (the tile plan precedes ev[0]).
+// bf16: the expert weights are bf16 without scales; xq is then the bf16
+// input x, hq receives bf16 h ([rows][I]) and xs, hs and the scale pointers
+// are unused.
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E,
                       int K, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
                       const float* xs, int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs,
-                      uint16_t* out, hipStream_t s, hipEvent_t* ev = nullptr);
+                      uint16_t* out, hipStream_t s, hipEvent_t* ev = nullptr, bool bf16 = false);
 
 // combine.hip
 hipError_t launch_combine(const int32_t* idx, const float* w, const int32_t* pair_row, const uint16_t* rows,

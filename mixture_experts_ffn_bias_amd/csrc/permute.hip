@@ -204,7 +204,7 @@ hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, i
                           int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s) {
   const int nchunks = (T + PERM_CHUNK - 1) / PERM_CHUNK;
   if (nchunks == 1) {
-    const int64_t nblocks = (int64_t)T * (d / BLK);
+    const int64_t nblocks = xq ? (int64_t)T * (d / BLK) : 0;  // no quantisation without xq
     const int64_t qblocks = (nblocks * 8 + PERM_CHUNK - 1) / PERM_CHUNK;
     hipLaunchKernelGGL(permute_small_kernel, dim3((unsigned)(1 + qblocks)), dim3(PERM_CHUNK), 0, s, idx, T, K, E,
                        counts, offsets, row_token, pair_row, x, nblocks, xq, xs);
@@ -218,7 +218,7 @@ hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, i
   hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(PERM_CHUNK), 0, s, idx, T, K, E, chunk_off, offsets,
                      row_token, pair_row);
   if ((err = hipGetLastError()) != hipSuccess) return err;
-  return launch_quant(x, T, d, xq, xs, s);
+  return xq ? launch_quant(x, T, d, xq, xs, s) : hipSuccess;
 }
 
 }  // namespace moe

@@ -179,15 +179,18 @@ def make_x(dims: Dims, tokens: int, device, seed: int, tag: int = 1) -> torch.Te
 
 
 def make_workload(name: str, device="cpu", tokens: Optional[int] = None, seed: Optional[int] = None,
-                  blocks: Optional[int] = None) -> Dict[str, object]:
-    """All inputs of a named workload.  Returns {"x", "blocks": [params...], ...}."""
+                  blocks: Optional[int] = None, weights: str = "e4m3") -> Dict[str, object]:
+    """All inputs of a named workload.  Returns {"x", "blocks": [params...], ...}.
+
+    weights: "e4m3" (the layer's FP8 experts) or "bf16" (the same laws, bf16 without scales).
+    """
     w = WORKLOADS[name]
     T = w.tokens if tokens is None else tokens
     s = w.seed if seed is None else seed
     nb = w.blocks if blocks is None else blocks
     out: Dict[str, object] = {"workload": w, "dims": w.dims, "tokens": T, "seed": s}
     out["x"] = make_x(w.dims, T, device, s)
-    out["blocks"] = [make_block(w.dims, w.bias, device, s, b) for b in range(nb)]
+    out["blocks"] = [make_block(w.dims, w.bias, device, s, b, weights=weights) for b in range(nb)]
     if w.blocks > 1:
         out["residual"] = _normal((T, w.dims.d_model), 1.0, device, s, 2).to(torch.bfloat16)
         out["gains"] = [1.0 + _normal((w.dims.d_model,), w.gain_sigma, device, s, 3 + 10 * b) for b in range(nb)]

@@ -29,6 +29,14 @@ def f64(t: torch.Tensor) -> np.ndarray:
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
+def to_numpy(t):
+    """Host copy of a tensor; bf16 comes back as its uint16 bit patterns."""
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
 class HostView:
     """Read-only mapping over device parameters that copies one expert at a time."""
 
@@ -37,11 +45,14 @@ class HostView:
             self.t = t
 
         def __getitem__(self, e):
-            return self.t[e].cpu().numpy()
+            return to_numpy(self.t[e])
 
     def __init__(self, params):
         self.p = params
         self.small = {k: params[k].cpu().numpy() for k in ("gate_w", "gate_b")}
+
+    def __contains__(self, k):
+        return k in self.p
 
     def __getitem__(self, k):
         if k in self.small:

@@ -21,7 +21,7 @@ FAKE = 1 << 20          # a 256-byte aligned non-null address; never dereference
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(moe_[a-z_]+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\**\s+\**(moe_[a-z_0-9]+)\s*\(", text, re.M)))
 
 
 def test_header_declares_the_expected_entry_points():
@@ -94,6 +94,8 @@ def test_zero_tokens_is_a_noop_everywhere():
     assert L.moe_forward(d, None, 0, None, None, None, None, None, 0, None) == 0
     assert L.moe_add_rmsnorm(7168, 0, None, None, None, 1e-6, None, None) == 0
     assert L.moe_mlp(7168, 18432, 0, None, None, None, None, 0, None) == 0
+    assert L.moe_grouped_ffn_bf16(d, 0, None, None, None, None, None, None, None, 0, None) == 0
+    assert L.moe_forward_bf16(d, None, 0, None, None, None, None, None, 0, None) == 0
 
 
 def test_null_pointers_rejected():
@@ -157,3 +159,25 @@ def test_mlp_argument_checks():
     small = moe.moe_mlp_workspace_size(7168, 2048, 64)
     assert L.moe_mlp(7168, 2048, 64, ctypes.byref(ex), FAKE, FAKE, FAKE, small - 1, None) == -3
     assert L.moe_mlp(7168, 2048, 64, ctypes.byref(ex), FAKE, FAKE, None, small, None) == -3
+
+
+def test_bf16_entry_points_reject_bad_arguments():
+    L = B.lib()
+    d = ctypes.byref(dims())
+    ex = moe.moe_experts_bf16(FAKE, FAKE, FAKE)
+    assert L.moe_grouped_ffn_bf16(d, 4, None, None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_grouped_ffn_bf16(d, 4, ctypes.byref(moe.moe_experts_bf16(FAKE, None, FAKE)), None, FAKE, FAKE, FAKE,
+                                  FAKE, FAKE, 1 << 30, None) == -1
+    assert L.moe_grouped_ffn_bf16(d, 4, ctypes.byref(moe.moe_experts_bf16(FAKE + 2, FAKE, FAKE)), None, FAKE, FAKE,
+                                  FAKE, FAKE, FAKE, 1 << 30, None) == -4
+    assert L.moe_grouped_ffn_bf16(d, 4, ctypes.byref(ex), None, FAKE, FAKE, FAKE + 2, FAKE, FAKE, 1 << 30, None) == -4
+    assert L.moe_grouped_ffn_bf16(d, 4, ctypes.byref(ex), None, FAKE, FAKE, FAKE, FAKE, None, 1 << 30, None) == -3
+    w = moe.moe_weights_bf16(FAKE, FAKE, ex, ex)
+    assert L.moe_forward_bf16(d, None, 4, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == -1
+    assert L.moe_forward_bf16(d, ctypes.byref(w), 4, None, FAKE, None, None, FAKE, 1 << 30, None) == -1
+    assert L.moe_forward_bf16(d, ctypes.byref(w), 4, FAKE, FAKE, None, None, FAKE, 16, None) == -3
+    assert L.moe_forward_bf16_timed(d, ctypes.byref(w), 4, FAKE, FAKE, None, None, FAKE, 1 << 30, None, None) == -1
+    bad = moe.moe_weights_bf16(FAKE, FAKE, moe.moe_experts_bf16(FAKE, FAKE, FAKE + 8), ex)
+    assert L.moe_forward_bf16(d, ctypes.byref(bad), 4, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == -4
+    # permute: xq and xs must be given together or not at all
+    assert L.moe_permute(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == -1

@@ -14,7 +14,7 @@ import torch
 import mixture_experts_ffn_bias_amd as moe
 import oracle
 import synth
-from _helpers import (HostView, assert_close, assert_rows_close, cdims, f64, metrics, routing_check,
+from _helpers import (HostView, assert_close, assert_rows_close, cdims, f64, metrics, routing_check, to_numpy,
                       weights_check)
 
 pytestmark = pytest.mark.gpu
@@ -26,7 +26,7 @@ def _say(msg):
 
 
 def _np_params(p):
-    return {k: v.cpu().numpy() for k, v in p.items()}
+    return {k: to_numpy(v) for k, v in p.items()}
 
 
 @pytest.fixture(scope="module")
@@ -495,3 +495,69 @@ def test_mlp_full_width_sampled_rows(T):
     ref = _mlp_ref(_np_params(p), f64(x)[rows])
     assert_rows_close(got[rows], ref, f"mlp full-width T={T}")
     assert np.isfinite(got).all()
+
+
+# ----------------------------------------------------------------------------
+# bf16 expert weights (Linear layers without scales, no activation quantisation)
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def tiny_params_bf16():
+    return synth.make_block(synth.TINY, "normal:0.1", DEV, seed=0, weights="bf16")
+
+
+def _bf16_expert(pn, pre, i):
+    return [oracle.bf16_weight(pn[pre + k][i]) for k in ("w1", "w3", "w2")]
+
+
+@pytest.mark.parametrize("T", [37, 300])
+def test_grouped_ffn_bf16_forced_routing_tiny(tiny_params_bf16, T):
+    _say(f"moe_grouped_ffn_bf16 tiny T={T}")
+    dims, p = synth.TINY, tiny_params_bf16
+    x = synth.make_x(dims, T, DEV, seed=40 + T)
+    K, E, d = dims.topk, dims.n_experts, dims.d_model
+    pn = _np_params(p)
+    xv = f64(x)
+    r = oracle.gate(xv, pn["gate_w"], pn["gate_b"], dims)
+    perm = oracle.permute(r["idx"], E)
+    rows_tok = np.concatenate([perm["row_token"], np.arange(T)]).astype(np.int32)
+    cd = cdims(dims)
+    out = torch.zeros((T * K + T, d), dtype=torch.bfloat16, device=DEV)
+    routed = moe.experts_struct_bf16(p["w1"], p["w3"], p["w2"])
+    shared = moe.experts_struct_bf16(p["sh_w1"], p["sh_w3"], p["sh_w2"])
+    moe.moe_grouped_ffn_bf16(cd, T, routed, shared, torch.from_numpy(perm["offsets"]).int().to(DEV),
+                             torch.from_numpy(rows_tok).to(DEV), x, out, moe.workspace(cd, T))
+    torch.cuda.synchronize()
+    got = f64(out)
+    ref = np.zeros_like(got)
+    off = perm["offsets"]
+    for e in range(E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size:
+            ref[rows] = oracle.expert_ffn_bf16(xv[perm["row_token"][rows]], *_bf16_expert(pn, "", e))
+    ref[T * K:] = oracle.expert_ffn_bf16(xv, *_bf16_expert(pn, "sh_", 0))
+    assert_rows_close(got, ref, f"grouped_ffn_bf16 tiny T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 37, 64, 1000])
+def test_forward_bf16_tiny(tiny_params_bf16, T):
+    _say(f"moe_forward_bf16 tiny T={T}")
+    dims = synth.TINY
+    x = synth.make_x(dims, T, DEV, seed=50 + T)
+    delta, gi, gw = run_forward(dims, tiny_params_bf16, x)
+    ref = oracle.moe_forward(f64(x), _np_params(tiny_params_bf16), dims)
+    same, _ = routing_check(gi, ref["routing"], dims)
+    weights_check(gi, gw, ref["routing"], same)
+    assert_close(f64(delta)[same], ref["y"][same], f"forward_bf16 tiny T={T}")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [64, 4096])
+def test_forward_bf16_full_shape(T):
+    _say(f"moe_forward_bf16 full shape T={T}")
+    p = synth.make_block(synth.FULL, "normal:0.01", DEV, seed=6, weights="bf16")
+    torch.cuda.synchronize()
+    _full_case(p, p["gate_b"], T, seed=110 + T, n_random=4)
+    del p
+    torch.cuda.empty_cache()
