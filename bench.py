@@ -1,7 +1,7 @@
 """Benchmark of the DeepSeek-V3.2-Exp MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|stack4|tiny]
-                    [--weights e4m3|bf16]
+                    [--weights e4m3|bf16] [--ep-share N]
 
 A step is one pass of the whole layer (router, permutation, grouped expert
 FFN, combine; for the stacked workload four blocks of fused residual-add
@@ -61,6 +61,12 @@ class HipEvents:
         if rc != 0:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return float(v.value)
+
+    def record(self, ev, stream):
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
 
     def close(self):
         for e in self.made:
@@ -210,6 +216,9 @@ def main():
     ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skewed", "stack4"])
     ap.add_argument("--weights", default="e4m3", choices=["e4m3", "bf16"],
                     help="expert weights: FP8 e4m3 with 128x128 block scales (the layer's), or bf16 without scales")
+    ap.add_argument("--ep-share", type=int, default=0, metavar="N",
+                    help="time one rank's share of an N-way expert-parallel layer instead: experts [0, E/N) "
+                         "plus the shared expert over all tokens (moe_forward_shard, fp32 partial output)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -238,6 +247,8 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 3}))
         return
+    if args.ep_share:
+        return bench_share(args, moe, synth, torch, np, dev)
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
     bf16 = args.weights == "bf16"
@@ -359,6 +370,75 @@ def main():
             out["cpu_baseline"]["sample"] += "; first block of the stack, so tokens/s per block"
         else:
             out["cpu_baseline"] = cpu_baseline(x0, data["blocks"][0], dims, args.cpu_budget, threads)
+    print(json.dumps(out), flush=True)
+
+
+def bench_share(args, moe, synth, torch, np, dev):
+    """One rank's share of an N-way expert-parallel layer: permutation, FFN of experts
+    [0, E/N) and of the shared expert, fp32 partial combine (the routing comes from the
+    gate, outside the timed region, as it would from the token's home rank)."""
+    wl = synth.WORKLOADS[args.workload]
+    dims = wl.dims
+    n = args.ep_share
+    if wl.blocks != 1 or dims.n_experts % n or args.weights != "e4m3":
+        sys.exit("--ep-share takes a single-block workload, a divisor of the expert count and e4m3 weights")
+    data = synth.make_workload(args.workload, device=dev)
+    T, p = data["tokens"], data["blocks"][0]
+    cd = moe.make_dims(dims.d_model, dims.n_experts, dims.n_groups, dims.topk_groups, dims.topk, dims.inter,
+                       dims.route_scale)
+    e_hi = dims.n_experts // n
+    keys = ("w1", "w3", "w2", "s1", "s3", "s2")
+    wts = moe.moe_weights(p["gate_w"].data_ptr(), p["gate_b"].data_ptr(),
+                          moe.experts_struct(*(p[k][:e_hi] for k in keys)),
+                          moe.experts_struct(*(p["sh_" + k] for k in keys)))
+    x = data["x"]
+    ws = moe.workspace(cd, T, device=dev)
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device=dev)
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device=dev)
+    moe.moe_gate(cd, T, x, p["gate_w"], p["gate_b"], idx, w, ws)
+    y = torch.empty((T, dims.d_model), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        moe.moe_forward_shard(cd, wts, T, 0, e_hi, True, x, idx, w, y, ws, stream)
+    hev = HipEvents()
+    K = args.steps
+    ev = hev.create(2 * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        hev.record(ev[2 * k], stream.cuda_stream)
+        moe.moe_forward_shard(cd, wts, T, 0, e_hi, True, x, idx, w, y, ws, stream)
+        hev.record(ev[2 * k + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = sum(hev.ms(ev[2 * k], ev[2 * k + 1]) for k in range(K)) / K
+    hev.close()
+    gi = idx.cpu().numpy()
+    touched = int((np.bincount(gi.ravel(), minlength=dims.n_experts)[:e_hi] > 0).sum())
+    d, I = dims.d_model, dims.inter
+    rows = int(((gi >= 0) & (gi < e_hi)).sum()) + T
+    wbytes = (touched + 1) * (3 * I * d + 3 * (I // 128) * (d // 128) * 4)
+    alg = wbytes + T * d * 2 + T * dims.topk * 8 + T * d * 4
+    flops = 2 * rows * 3 * d * I
+    gbs = alg / (step_ms * 1e-3) / 1e9
+    tfs = flops / (step_ms * 1e-3) / 1e12
+    if gbs / HBM_PEAK_GBS >= tfs / BF16_MFMA_PEAK_TFLOPS:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4)}
+    roof.update({"kernel": "share step (permute + FFN + partial combine)", "traffic": None,
+                 "launch_ms": round(step_ms, 4), "alg_bytes": int(alg), "alg_flops": int(flops)})
+    out = {
+        "metric": "MoE layer tokens/s (d7168,256e,top8): one rank's expert share",
+        "value": round(T * K / wall, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "ep_share": f"experts 0..{e_hi - 1} of "
+                   f"{dims.n_experts} + shared ({n}-way split)", "rows": rows, "touched_experts": touched},
+        "roofline": roof, "cpu_baseline": None,
+    }
     print(json.dumps(out), flush=True)
 
 

@@ -211,6 +211,26 @@ int moe_forward_bf16_timed(const moe_dims* dims, const moe_weights_bf16* weights
                            void* workspace, size_t workspace_bytes, void* stream,
                            void* const* stage_events);
 
+/* One rank's share of an expert-parallel layer ("MoE update", moe-forward
+ * excerpt: a rank runs only experts [experts_start_idx, experts_end_idx) and
+ * the ranks' y are summed by an all-reduce before the cast to the input dtype).
+ *   expert_begin, expert_end  the rank's routed experts, 0 <= begin < end <= E
+ *   weights->routed           holds exactly those end - begin experts, expert_begin first
+ *   with_shared               1: add the shared expert (one rank of the group does);
+ *                             0: weights->shared is not read
+ *   x      bf16 [T][d]  all tokens (16-byte aligned)
+ *   idx, w int32 / fp32 [T][K]  the routing of every token (moe_gate)
+ *   y_partial  fp32 [T][d] out: sum over k with idx[t][k] in [begin, end), in ascending
+ *              expert id, of w[t][k] * expert(x[t]) (+ the shared expert), fp32, unrounded
+ *              (16-byte aligned)
+ * Summing y_partial over ranks that cover [0, E) once (the shared expert on one of
+ * them) and rounding to bf16 gives moe_forward's output up to the fp32 order of the
+ * cross-rank sum.  Needs moe_workspace_size(dims, T). */
+int moe_forward_shard(const moe_dims* dims, const moe_weights* weights, int64_t tokens,
+                      int32_t expert_begin, int32_t expert_end, int32_t with_shared,
+                      const uint16_t* x, const int32_t* idx, const float* w, float* y_partial,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Fused residual add + RMSNorm ("MoE update", rmsnorm excerpt, residual branch):
  *   r = float(x) + float(residual);  residual <- bf16(r);
  *   out = bf16(gain * r * rsqrt(mean(r^2) + eps))

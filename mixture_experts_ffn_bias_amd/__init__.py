@@ -7,7 +7,7 @@ package is its Python binding.
 from ._binding import (  # noqa: F401
     LIB_PATH, MOE_FORWARD_EVENTS, SYMBOLS, MoeError, MoELayer, experts_struct, experts_struct_bf16, lib, make_dims,
     moe_add_rmsnorm, moe_combine, moe_dims, moe_experts, moe_experts_bf16, moe_forward, moe_forward_bf16,
-    moe_forward_bf16_timed, moe_forward_timed, moe_gate, moe_grouped_ffn, moe_grouped_ffn_bf16, moe_mlp,
+    moe_forward_bf16_timed, moe_forward_shard, moe_forward_timed, moe_gate, moe_grouped_ffn, moe_grouped_ffn_bf16, moe_mlp,
     moe_mlp_workspace_size, moe_permute, moe_weights, moe_weights_bf16, moe_workspace_size, mlp_workspace,
     status_string, workspace,
 )

@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK = 0
 SYMBOLS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_bf16", "moe_combine",
-           "moe_forward", "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_add_rmsnorm",
+           "moe_forward", "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_forward_shard",
+           "moe_add_rmsnorm",
            "moe_mlp_workspace_size", "moe_mlp", "moe_status_string")
 MOE_FORWARD_EVENTS = 6
 
@@ -80,12 +81,14 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_bf16.argtypes = [dp, ctypes.POINTER(moe_weights_bf16), i64, vp, vp, vp, vp, vp, sz, vp]
         L.moe_forward_bf16_timed.argtypes = [dp, ctypes.POINTER(moe_weights_bf16), i64, vp, vp, vp, vp, vp, sz, vp,
                                              ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_forward_shard.argtypes = [dp, ctypes.POINTER(moe_weights), i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_add_rmsnorm.argtypes = [i32, i64, vp, vp, vp, ctypes.c_float, vp, vp]
         L.moe_mlp_workspace_size.argtypes = [i32, i32, i64]
         L.moe_mlp_workspace_size.restype = sz
         L.moe_mlp.argtypes = [i32, i32, i64, ctypes.POINTER(moe_experts), vp, vp, vp, sz, vp]
         for n in ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_bf16", "moe_combine", "moe_forward",
-                  "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_add_rmsnorm", "moe_mlp"):
+                  "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_forward_shard",
+                  "moe_add_rmsnorm", "moe_mlp"):
             getattr(L, n).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -199,6 +202,13 @@ def moe_forward_bf16_timed(dims, weights: moe_weights_bf16, tokens, x, delta, id
     _check(lib().moe_forward_bf16_timed(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta),
                                         _p(idx_out), _p(w_out), _p(ws), ws.numel() if ws is not None else 0,
                                         _stream(stream), arr), "moe_forward_bf16_timed")
+
+
+def moe_forward_shard(dims, weights: moe_weights, tokens, expert_begin, expert_end, with_shared, x, idx, w, y_partial,
+                      ws, stream=None):
+    _check(lib().moe_forward_shard(ctypes.byref(dims), ctypes.byref(weights), int(tokens), int(expert_begin),
+                                   int(expert_end), 1 if with_shared else 0, _p(x), _p(idx), _p(w), _p(y_partial),
+                                   _p(ws), ws.numel() if ws is not None else 0, _stream(stream)), "moe_forward_shard")
 
 
 def moe_add_rmsnorm(d, tokens, x, residual, gain, eps, out, stream=None):

@@ -364,6 +364,43 @@ int moe_forward_bf16_timed(const moe_dims* dims, const moe_weights_bf16* weights
                       (hipStream_t)stream, ev);
 }
 
+int moe_forward_shard(const moe_dims* dims, const moe_weights* weights, int64_t tokens, int32_t expert_begin,
+                      int32_t expert_end, int32_t with_shared, const uint16_t* x, const int32_t* idx, const float* w,
+                      float* y_partial, void* workspace, size_t workspace_bytes, void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  const moe_dims& d = *dims;
+  if (expert_begin < 0 || expert_end > d.n_experts || expert_begin >= expert_end) return MOE_ERR_INVALID_ARG;
+  if (tokens == 0) return MOE_OK;
+  if (!weights || !x || !idx || !w || !y_partial) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_experts(&weights->routed));
+  if (with_shared) MOE_TRY(check_experts(&weights->shared));
+  if (!aligned(x, 16) || !aligned(y_partial, 16) || !aligned(idx, 4) || !aligned(w, 4)) return MOE_ERR_ALIGN;
+  const Layout L = layout(d, tokens);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
+  const hipStream_t s = (hipStream_t)stream;
+  const int T = (int)tokens;
+  int32_t* offsets = at<int32_t>(workspace, L.offsets);
+  int32_t* row_token = at<int32_t>(workspace, L.row_token);
+  int32_t* pair_row = at<int32_t>(workspace, L.pair_row);
+  uint8_t* xq = at<uint8_t>(workspace, L.xq);
+  float* xs = at<float>(workspace, L.xs);
+  uint16_t* rows = at<uint16_t>(workspace, L.rows);
+  MOE_TRY(hip_status(launch_permute(idx, x, T, d.d_model, d.n_experts, d.topk, at<int32_t>(workspace, L.chunk_cnt),
+                                    at<int32_t>(workspace, L.chunk_off), at<int32_t>(workspace, L.counts), offsets,
+                                    row_token, pair_row, xq, xs, s)));
+  const ExpertPtrs rp = ptrs(weights->routed);
+  ExpertPtrs sp;
+  if (with_shared) sp = ptrs(weights->shared);
+  MOE_TRY(hip_status(launch_ffn(rp, with_shared ? &sp : nullptr, T, d.d_model, d.inter, d.n_experts, d.topk, offsets,
+                                row_token, xq, xs, at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
+                                at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), rows, s, nullptr, false,
+                                expert_begin, expert_end)));
+  return hip_status(launch_combine_partial(idx, w, pair_row, rows, with_shared ? 1 : 0, T, d.topk, expert_begin,
+                                           expert_end, d.d_model, y_partial, s));
+}
+
 int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* residual, const float* gain, float eps,
                     uint16_t* out, void* stream) {
   if (d <= 0 || tokens < 0 || !(eps >= 0.f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;

@@ -42,14 +42,23 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
 // bf16: the expert weights are bf16 without scales; xq is then the bf16
 // input x, hq receives bf16 h ([rows][I]) and xs, hs and the scale pointers
 // are unused.
+// [e_lo, e_hi) (e_hi < 0: E): the routed experts to run; `routed` then holds
+// exactly those experts (expert e_lo first).  Rows of other experts are left
+// untouched.
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E,
                       int K, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
                       const float* xs, int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs,
-                      uint16_t* out, hipStream_t s, hipEvent_t* ev = nullptr, bool bf16 = false);
+                      uint16_t* out, hipStream_t s, hipEvent_t* ev = nullptr, bool bf16 = false,
+                      int e_lo = 0, int e_hi = -1);
 
 // combine.hip
 hipError_t launch_combine(const int32_t* idx, const float* w, const int32_t* pair_row, const uint16_t* rows,
                           int has_shared, int T, int K, int E, int d, uint16_t* delta, hipStream_t s);
+// The fp32 partial sum of the experts in [e_lo, e_hi) (+ the shared rows when
+// has_shared), in ascending expert order, without the final bf16 rounding.
+hipError_t launch_combine_partial(const int32_t* idx, const float* w, const int32_t* pair_row,
+                                  const uint16_t* rows, int has_shared, int T, int K, int e_lo, int e_hi, int d,
+                                  float* y, hipStream_t s);
 
 // norm.hip
 hipError_t launch_add_rmsnorm(const uint16_t* x, uint16_t* residual, const float* gain, float eps, int d,

@@ -181,3 +181,23 @@ def test_bf16_entry_points_reject_bad_arguments():
     assert L.moe_forward_bf16(d, ctypes.byref(bad), 4, FAKE, FAKE, None, None, FAKE, 1 << 30, None) == -4
     # permute: xq and xs must be given together or not at all
     assert L.moe_permute(d, 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == -1
+
+
+def test_shard_argument_checks():
+    L = B.lib()
+    d = ctypes.byref(dims())
+    ex = moe.moe_experts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    w = moe.moe_weights(FAKE, FAKE, ex, ex)
+    call = lambda b, e, sh, x=FAKE, idx=FAKE, y=FAKE, ws=1 << 30, T=4, wt=ctypes.byref(w): L.moe_forward_shard(
+        d, wt, T, b, e, sh, x, idx, FAKE, y, FAKE if ws else None, ws, None)
+    assert call(0, 0, 1) == -1           # empty range
+    assert call(32, 16, 1) == -1         # reversed range
+    assert call(-1, 16, 1) == -1
+    assert call(0, 257, 1) == -1         # past the last expert
+    assert call(0, 32, 1, T=0) == 0      # no tokens: no-op
+    assert call(0, 32, 1, idx=None) == -1
+    assert call(0, 32, 1, wt=None) == -1
+    assert call(0, 32, 1, y=FAKE + 4) == -4
+    assert call(0, 32, 1, ws=0) == -3
+    noshared = moe.moe_weights(FAKE, FAKE, ex, moe.moe_experts(None, None, None, None, None, None))
+    assert call(0, 32, 1, wt=ctypes.byref(noshared)) == -1   # the shared expert is required with with_shared

@@ -561,3 +561,88 @@ def test_forward_bf16_full_shape(T):
     _full_case(p, p["gate_b"], T, seed=110 + T, n_random=4)
     del p
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------
+# one rank's share of an expert-parallel layer (experts [b, e) + fp32 partial)
+# ----------------------------------------------------------------------------
+
+def _shard_weights(p, b, e, with_shared):
+    keys = ("w1", "w3", "w2", "s1", "s3", "s2")
+    routed = moe.experts_struct(*(p[k][b:e] for k in keys))      # views: the rank holds experts b..e-1
+    shared = moe.experts_struct(*(p["sh_" + k] for k in keys)) if with_shared else moe.moe_experts()
+    return moe.moe_weights(p["gate_w"].data_ptr(), p["gate_b"].data_ptr(), routed, shared)
+
+
+def _oracle_partial(pv, xv, tok, idx, w, b, e, with_shared):
+    """sum over the token's choices with expert in [b, e), ascending expert, of w * expert(x) (+ shared)."""
+    y = np.zeros((tok.size, xv.shape[1]))
+    for ex in range(b, e):
+        rows, ks = np.nonzero(idx[tok] == ex)
+        if rows.size:
+            o = oracle.expert_ffn(xv[tok[rows]], *(np.asarray(pv[k][ex]) for k in ("w1", "s1", "w3", "s3", "w2", "s2")))
+            y[rows] += o * w[tok[rows], ks][:, None].astype(np.float64)
+    if with_shared:
+        y += oracle.expert_ffn(xv[tok], *(np.asarray(pv["sh_" + k][0]) for k in ("w1", "s1", "w3", "s3", "w2", "s2")))
+    return y
+
+
+def test_shards_sum_to_the_layer_tiny(tiny_params):
+    _say("moe_forward_shard tiny: 4 shards of 4 experts, T=300")
+    dims, p = synth.TINY, tiny_params
+    T = 300
+    cd = cdims(dims)
+    x = synth.make_x(dims, T, DEV, seed=60)
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device=DEV)
+    ws = moe.workspace(cd, T)
+    moe.moe_gate(cd, T, x, p["gate_w"], p["gate_b"], idx, w, ws)
+    delta = torch.empty_like(x)
+    moe.moe_forward(cd, moe.MoELayer(cd, p).weights, T, x, delta, None, None, ws)
+    pn, xv = _np_params(p), f64(x)
+    gi, gw = idx.cpu().numpy().astype(np.int64), w.cpu().numpy()
+    total = np.zeros((T, dims.d_model))
+    for s in range(4):
+        b, e = 4 * s, 4 * s + 4
+        y = torch.full((T, dims.d_model), float("nan"), dtype=torch.float32, device=DEV)
+        moe.moe_forward_shard(cd, _shard_weights(p, b, e, s == 0), T, b, e, s == 0, x, idx, w, y, ws)
+        torch.cuda.synchronize()
+        got = y.cpu().numpy().astype(np.float64)
+        assert np.isfinite(got).all()
+        ref = _oracle_partial(pn, xv, np.arange(T), gi, gw, b, e, s == 0)
+        assert_close(got, ref, f"shard {s} (experts {b}..{e - 1})")
+        total += got
+    # the cross-rank sum, rounded once, is the layer output (up to the fp32 order of the sum)
+    d_sum = torch.from_numpy(total).float().to(torch.bfloat16).double().numpy()
+    d_full = f64(delta)
+    ulp = np.abs(d_full) * 2.0 ** -7 + 1e-30
+    assert (np.abs(d_sum - d_full) <= ulp).mean() > 0.999
+    assert_close(total, oracle.moe_forward(xv, pn, dims, idx=gi)["y"], "sum of shards vs oracle layer")
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_shard_one_group_full_shape(full_params):
+    """One rank holding one group of 32 experts (group 1), no shared expert, T=4096."""
+    _say("moe_forward_shard full shape, experts 32..63, T=4096")
+    dims, p = synth.FULL, full_params
+    T, b, e = 4096, 32, 64
+    cd = cdims(dims)
+    x = synth.make_x(dims, T, DEV, seed=120)
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device=DEV)
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device=DEV)
+    ws = moe.workspace(cd, T)
+    moe.moe_gate(cd, T, x, p["gate_w"], p["gate_b"], idx, w, ws)
+    y = torch.full((T, dims.d_model), float("nan"), dtype=torch.float32, device=DEV)
+    moe.moe_forward_shard(cd, _shard_weights(p, b, e, False), T, b, e, False, x, idx, w, y, ws)
+    torch.cuda.synchronize()
+    gi, gw = idx.cpu().numpy().astype(np.int64), w.cpu().numpy()
+    got = y.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    hit = np.nonzero(((gi >= b) & (gi < e)).any(1))[0]
+    miss = np.nonzero(~((gi >= b) & (gi < e)).any(1))[0]
+    assert np.all(got[miss] == 0.0)                        # tokens routed elsewhere get nothing
+    rng = np.random.default_rng(7)
+    tok = np.sort(rng.choice(hit, min(10, hit.size), replace=False))
+    ref = _oracle_partial(HostView(p), f64(x), tok, gi, gw, b, e, False)
+    assert_close(got[tok], ref, f"shard experts {b}..{e - 1} full shape ({tok.size} sampled tokens)")
