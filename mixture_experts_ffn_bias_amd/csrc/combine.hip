@@ -4,9 +4,10 @@
 // shared_experts(x)``, then the cast back to the input dtype;
 // "DeepSeek-V3.2-Exp · Add shared output", formula).
 //
-// One workgroup per token; the token's K rows are visited in ascending
-// expert id, so the fp32 sum has the same order as the pages' loop and the
-// result is deterministic (no atomics).
+// One workgroup per token and share of the row (small batches split each row
+// over several workgroups to occupy the chip); the token's K rows are visited
+// in ascending expert id, so the fp32 sum has the same order as the pages'
+// loop and the result is deterministic (no atomics).
 //
 // The partial form serves one rank of an expert-parallel layer: it sums only
 // the experts [e_lo, e_hi) a rank holds (the pages' experts_start_idx ..
@@ -62,8 +63,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
   }
   __syncthreads();
   const int n = s_n;
+  // this workgroup's share of the row: 8-element chunks [c0, c1)
   const int nch = d / 8;
-  for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+  const int per = (nch + gridDim.y - 1) / gridDim.y;
+  const int c0 = blockIdx.y * per, c1 = min(nch, c0 + per);
+  for (int c = c0 + threadIdx.x; c < c1; c += blockDim.x) {
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.f;
@@ -103,18 +107,30 @@ __global__ __launch_bounds__(256) void combine_kernel(const int32_t* __restrict_
 
 }  // namespace
 
+namespace {
+
+// workgroups per token: enough to cover the chip's 256 CUs at small T, with
+// at least 64 eight-element chunks each
+unsigned combine_split(int T, int d) {
+  int sp = 1;
+  while (T * sp < 512 && sp < 8 && d / 8 / (2 * sp) >= 64) sp *= 2;
+  return (unsigned)sp;
+}
+
+}  // namespace
+
 hipError_t launch_combine(const int32_t* idx, const float* w, const int32_t* pair_row, const uint16_t* rows,
                           int has_shared, int T, int K, int E, int d, uint16_t* delta, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel<false>, dim3(T), dim3(256), 0, s, idx, w, pair_row, rows, has_shared, T, K, 0, E,
-                     d, (void*)delta);
+  hipLaunchKernelGGL(combine_kernel<false>, dim3(T, combine_split(T, d)), dim3(256), 0, s, idx, w, pair_row, rows,
+                     has_shared, T, K, 0, E, d, (void*)delta);
   return hipGetLastError();
 }
 
 hipError_t launch_combine_partial(const int32_t* idx, const float* w, const int32_t* pair_row,
                                   const uint16_t* rows, int has_shared, int T, int K, int e_lo, int e_hi, int d,
                                   float* y, hipStream_t s) {
-  hipLaunchKernelGGL(combine_kernel<true>, dim3(T), dim3(256), 0, s, idx, w, pair_row, rows, has_shared, T, K, e_lo,
-                     e_hi, d, (void*)y);
+  hipLaunchKernelGGL(combine_kernel<true>, dim3(T, combine_split(T, d)), dim3(256), 0, s, idx, w, pair_row, rows,
+                     has_shared, T, K, e_lo, e_hi, d, (void*)y);
   return hipGetLastError();
 }
 

@@ -14,6 +14,8 @@ namespace moe {
 
 namespace {
 
+constexpr int GATE_KSPLIT_MAX = 16;  // K splits of the logits (partials the selection adds)
+
 __device__ __forceinline__ void split3(float w, __bf16& hi, __bf16& mid, __bf16& lo) {
   const uint32_t u = __float_as_uint(w);
   const float h = __uint_as_float(u & 0xFFFF0000u);     // top 8 significant bits
@@ -26,20 +28,20 @@ __device__ __forceinline__ void split3(float w, __bf16& hi, __bf16& mid, __bf16&
   lo = (__bf16)r2;
 }
 
-// Grid (ceil(T/64), ceil(E/64), ksplit), 256 threads.  Wave w owns tokens
-// [t0, t0+16) and up to four 16-expert tiles; blockIdx.z a K range.
-// zpart[z][t][e] receives the partial logits of that K range.
+// Grid (ceil(T/64), ceil(E/(16 ntw)), ksplit), 256 threads.  Wave w owns
+// tokens [t0, t0+16) and up to ntw (1..4) 16-expert tiles; blockIdx.z a K
+// range.  zpart[z][t][e] receives the partial logits of that K range.
 __global__ __launch_bounds__(256) void gate_logits_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ gw,
                                                           float* __restrict__ zpart, int T, int d, int E,
-                                                          int kchunk) {
+                                                          int kchunk, int ntw) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int t0 = blockIdx.x * 64 + wave * 16;
-  const int e0 = blockIdx.y * 64;
+  const int e0 = blockIdx.y * 16 * ntw;
   const int k0 = blockIdx.z * kchunk;
   const int k1 = min(d, k0 + kchunk);
   if (t0 >= T) return;  // no barriers in this kernel
-  const int nt = min(4, (E - e0) >> 4);
+  const int nt = min(ntw, (E - e0) >> 4);
   const uint16_t* xr = x + (size_t)min(t0 + r, T - 1) * d;
   const float* wr[4];
 #pragma unroll
@@ -247,13 +249,23 @@ __global__ __launch_bounds__(256) void gate_select_kernel(const float* __restric
 
 }  // namespace
 
+namespace {
+
+// 16-expert tiles per wave of the logits kernel: small batches spread the
+// router weight over more workgroups (experts) instead of more K splits, which
+// keeps the partial logits the selection has to add small.
+int gate_tiles_per_wave(int64_t T) { return T <= 256 ? 1 : 4; }
+
+}  // namespace
+
 int gate_ksplit(int64_t T, int d, int E) {
-  int64_t base = ((T + 63) / 64) * ((E + 63) / 64);
+  const int ntw = gate_tiles_per_wave(T);
+  int64_t base = ((T + 63) / 64) * ((E + 16 * ntw - 1) / (16 * ntw));
   if (base < 1) base = 1;
   int64_t ks = (512 + base - 1) / base;
   const int ksteps = d / 32;
   if (ks > ksteps) ks = ksteps;
-  if (ks > 64) ks = 64;
+  if (ks > GATE_KSPLIT_MAX) ks = GATE_KSPLIT_MAX;
   if (ks < 1) ks = 1;
   return (int)ks;
 }
@@ -264,8 +276,9 @@ hipError_t launch_gate(const uint16_t* x, const float* gate_w, const float* gate
   const int ksteps = d / 32;
   const int kchunk = ((ksteps + ksplit - 1) / ksplit) * 32;
   const int kz = (d + kchunk - 1) / kchunk;
-  dim3 grid((T + 63) / 64, (E + 63) / 64, kz);
-  hipLaunchKernelGGL(gate_logits_kernel, grid, dim3(256), 0, s, x, gate_w, zpart, T, d, E, kchunk);
+  const int ntw = gate_tiles_per_wave(T);
+  dim3 grid((T + 63) / 64, (E + 16 * ntw - 1) / (16 * ntw), kz);
+  hipLaunchKernelGGL(gate_logits_kernel, grid, dim3(256), 0, s, x, gate_w, zpart, T, d, E, kchunk, ntw);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (kz >= 8 && T <= 1024)
