@@ -105,15 +105,30 @@ struct FfnArgs {
 // that the L2 can serve the repeat reads.
 // ---------------------------------------------------------------------------
 
-constexpr int TT_ROWS = 128;                 // activation rows per tile
 constexpr int TT_WROWS = 256;                // weight rows per tile
 constexpr int TT_A_BYTES = TT_WROWS * BLK;   // one K block of the weight tile
-constexpr int TT_B_BYTES = TT_ROWS * BLK;    // one K block of the activation tile
-constexpr int TT_S_BYTES = TT_ROWS * 4;      // activation scales of one K block
-constexpr int TT_STAGE = TT_A_BYTES + TT_B_BYTES + TT_S_BYTES;
-constexpr int TT_NSTAGE = 3;
-constexpr int TT_SMEM = TT_NSTAGE * TT_STAGE;
 constexpr int CPOL_NT = 2;                   // cache-policy bits of a non-temporal load (gfx94x/gfx950)
+
+// Shape of the LDS pipeline for tiles of ROWS activation rows.  A stage holds
+// one K block: the 256 weight rows, the ROWS activation rows and their scales.
+//   ROWS = 128: three stages (two K blocks in flight), one workgroup per CU.
+//   ROWS = 32 (small batches, where the weights are the traffic): two stages
+//     of 36 KiB and at most 128 VGPRs, so two workgroups share a CU and one's
+//     start-up and epilogue overlap the other's weight stream.
+template <int ROWS>
+struct Tile {
+  static_assert(ROWS == 32 || ROWS == 128, "tile rows");
+  static constexpr int B_BYTES = ROWS * BLK;
+  static constexpr int S_BYTES = ROWS * 4;
+  static constexpr int STAGE = TT_A_BYTES + B_BYTES + S_BYTES;
+  static constexpr int NSTAGE = ROWS == 128 ? 3 : 2;
+  static constexpr int SMEM = NSTAGE * STAGE;
+  static constexpr int OCC = ROWS == 128 ? 1 : 2;       // workgroups per CU (8 waves each: 2 OCC waves per SIMD)
+  static constexpr int APW = ROWS == 128 ? 2 : 1;       // 8-row activation pieces per copying wave
+  static constexpr int AWAVES = ROWS / (8 * APW);       // waves that copy activation rows
+  static constexpr int SWAVES = (ROWS + 63) / 64;       // waves that copy activation scales (64 rows each)
+  static constexpr int MVMAX = ROWS >= 64 ? 4 : ROWS / 16;  // 16-row sub-tiles per wave
+};
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 typedef __attribute__((address_space(1))) void* gbl_ptr_t;
@@ -135,20 +150,29 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Global -> LDS copies (global_load_lds) of one K block.  Wave w copies
-// weight rows [32w, 32w + 32) (four 8-row pieces), activation rows
-// [16w, 16w + 16) (two pieces) and, for w < 2, the scales of activation rows
-// [64w, 64w + 64).  Lane l of a piece covers row piece_row0 + l/8 and LDS slot
-// l%8, so it fetches global chunk (l%8) ^ swz(row).
+// weight rows [32w, 32w + 32) (four 8-row pieces), the APW 8-row activation
+// pieces [APW w, APW w + APW) (waves w < AWAVES) and, e4m3 only, for
+// w < SWAVES the scales of activation rows [64w, 64w + 64).  Lane l of a
+// piece covers row piece_row0 + l/8 and LDS slot l%8, so it fetches global
+// chunk (l%8) ^ swz(row).
+template <int ROWS>
 struct TileSrc {
-  const uint8_t* a[4];  // this lane's source rows for the four weight pieces (chunk applied)
-  const uint8_t* b[2];  // ... for the two activation pieces
-  const float* s;       // scale row of activation row 64w + lane (waves 0, 1)
+  const uint8_t* a[4];                // this lane's source rows for the four weight pieces (chunk applied)
+  const uint8_t* b[Tile<ROWS>::APW];  // ... for this wave's activation pieces
+  const float* s;                     // scale row of activation row 64w + lane (waves w < SWAVES)
 };
 
-// act (wave-uniform): this wave's activation rows [16w, 16w + 16) hold tile
-// rows; otherwise no MFMA reads them and they are not copied.
-template <bool BF, int WPOL>
-__device__ __forceinline__ void tile_issue(const TileSrc& src, uint8_t* stage, int kb, int wave, bool act) {
+// act (wave-uniform): this wave's activation pieces hold rows some MFMA
+// reads; otherwise they are not copied.
+template <int ROWS, bool BF>
+__device__ __forceinline__ int tile_copies(int wave, bool act) {
+  using G = Tile<ROWS>;
+  return 4 + (act ? G::APW : 0) + (!BF && wave < G::SWAVES ? 1 : 0);
+}
+
+template <int ROWS, bool BF, int WPOL>
+__device__ __forceinline__ void tile_issue(const TileSrc<ROWS>& src, uint8_t* stage, int kb, int wave, bool act) {
+  using G = Tile<ROWS>;
   const int off = kb * BLK;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -156,32 +180,30 @@ __device__ __forceinline__ void tile_issue(const TileSrc& src, uint8_t* stage, i
                                      WPOL);
   if (act) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < G::APW; ++j)
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[j] + off),
-                                       (lds_ptr_t)(stage + TT_A_BYTES + (wave * 2 + j) * 1024), 16, 0, 0);
+                                       (lds_ptr_t)(stage + TT_A_BYTES + (wave * G::APW + j) * 1024), 16, 0, 0);
   }
-  if (!BF && wave < 2)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.s + kb), (lds_ptr_t)(stage + TT_A_BYTES + TT_B_BYTES + wave * 256),
-                                     4, 0, 0);
+  if (!BF && wave < G::SWAVES) {
+    if (ROWS >= 64 || (threadIdx.x & 63) < ROWS)
+      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.s + kb),
+                                       (lds_ptr_t)(stage + TT_A_BYTES + G::B_BYTES + wave * 256), 4, 0, 0);
+  }
 }
 
-// Wait until this wave's copies of every stage but the newest one have
-// landed: the newest stage's copies are the 4 weight pieces, 2 activation
-// pieces when `act`, and (e4m3 only) one scale copy on waves 0 and 1.
-template <bool BF>
-__device__ __forceinline__ void tile_wait_all_but_newest(int wave, bool newest_issued, bool act) {
-  if (!newest_issued) {
-    wait_vmcnt<0>();
-  } else if (!BF && wave < 2) {
-    if (act)
-      wait_vmcnt<7>();
-    else
-      wait_vmcnt<5>();
-  } else {
-    if (act)
-      wait_vmcnt<6>();
-    else
-      wait_vmcnt<4>();
+// Wait until at most n of this wave's vector-memory operations are pending
+// (n wave-uniform, 0 <= n <= 14; larger values wait for all).
+__device__ __forceinline__ void wait_vmcnt_upto(int n) {
+  switch (__builtin_amdgcn_readfirstlane(n)) {
+    case 4: wait_vmcnt<4>(); break;
+    case 5: wait_vmcnt<5>(); break;
+    case 6: wait_vmcnt<6>(); break;
+    case 7: wait_vmcnt<7>(); break;
+    case 8: wait_vmcnt<8>(); break;
+    case 10: wait_vmcnt<10>(); break;
+    case 12: wait_vmcnt<12>(); break;
+    case 14: wait_vmcnt<14>(); break;
+    default: wait_vmcnt<0>(); break;
   }
 }
 
@@ -211,29 +233,42 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
 // (0..4; a compile-time count keeps the K-block body free of branches, so the
 // LDS reads, decodes and MFMAs of a block can be interleaved).  WPOL: cache
 // policy of the weight copies.
-template <bool BF, int MV, int WPOL>
-__device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src, const_f32_ptr sa0,
-                                               const_f32_ptr sa1, int nkb, int nrows, v4f (&acc)[2][2][4]) {
+template <int ROWS, bool BF, int MV, int WPOL>
+__device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS>& src, const_f32_ptr sa0,
+                                               const_f32_ptr sa1, int nkb, int nrows,
+                                               v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
+  using G = Tile<ROWS>;
+  constexpr int AHEAD = G::NSTAGE - 1;  // K blocks whose copies are in flight during a multiply
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
 
-  const bool act = 16 * wave < nrows;
-  tile_issue<BF, WPOL>(src, smem, 0, wave, act);
-  if (nkb > 1) tile_issue<BF, WPOL>(src, smem + TT_STAGE, 1, wave, act);
-  tile_wait_all_but_newest<BF>(wave, nkb > 1, act);
+  const bool act = wave < G::AWAVES && 16 * ((wave * G::APW * 8) >> 4) < nrows;
+  const int per_stage = tile_copies<ROWS, BF>(wave, act);
+  int issued = 0;
+#pragma unroll
+  for (int k = 0; k < AHEAD; ++k) {
+    if (k < nkb) {
+      tile_issue<ROWS, BF, WPOL>(src, smem + k * G::STAGE, k, wave, act);
+      ++issued;
+    }
+  }
+  wait_vmcnt_upto(per_stage * (issued - 1));
   pipeline_barrier();
 
+  // Iteration kb issues the copies of block kb + AHEAD into the stage that
+  // block kb - 1 used (every wave left it at the last barrier), multiplies
+  // block kb, then waits for its own copies of block kb + 1 (all but those of
+  // the blocks issued after it); the barrier publishes that stage.
   int cur = 0;  // stage buffer holding K block kb
   for (int kb = 0; kb < nkb; ++kb) {
-    const bool ahead = kb + 2 < nkb;
-    if (ahead) {
-      const int nb = cur == 0 ? 2 : cur - 1;  // (kb + 2) % 3
-      tile_issue<BF, WPOL>(src, smem + nb * TT_STAGE, kb + 2, wave, act);
+    if (kb + AHEAD < nkb) {
+      const int nb = cur == 0 ? G::NSTAGE - 1 : cur - 1;  // (kb + AHEAD) % NSTAGE
+      tile_issue<ROWS, BF, WPOL>(src, smem + nb * G::STAGE, kb + AHEAD, wave, act);
     }
     // a wave whose 64 rows hold no tile row (MV = 0) only helps with the copies
     if constexpr (BF && MV > 0) {
       // bf16 operands: the 128 bytes of a row are 64 k values, two MFMAs per block, no scales
-      const uint8_t* la = smem + cur * TT_STAGE;
+      const uint8_t* la = smem + cur * G::STAGE;
       const uint8_t* lb = la + TT_A_BYTES;
       FragH B[MV];
 #pragma unroll
@@ -252,9 +287,9 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src
       }
     }
     if constexpr (!BF && MV > 0) {
-      const uint8_t* la = smem + cur * TT_STAGE;
+      const uint8_t* la = smem + cur * G::STAGE;
       const uint8_t* lb = la + TT_A_BYTES;
-      const float* ls = (const float*)(lb + TT_B_BYTES);
+      const float* ls = (const float*)(lb + G::B_BYTES);
       const float s_a0 = sa0[kb], s_a1 = sa1[kb];
       Frag B[MV];
       float sb[MV];
@@ -286,64 +321,77 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc& src
         }
       }
     }
-    if (kb + 1 < nkb) tile_wait_all_but_newest<BF>(wave, ahead, act);
+    if (kb + 1 < nkb) wait_vmcnt_upto(per_stage * (min(kb + AHEAD, nkb - 1) - kb - 1));
     pipeline_barrier();
-    cur = cur == 2 ? 0 : cur + 1;
+    cur = cur == G::NSTAGE - 1 ? 0 : cur + 1;
   }
 }
 
-template <bool BF, int WPOL>
-__device__ __forceinline__ void run_mainloop_pol(uint8_t* smem, const TileSrc& src, const_f32_ptr c0, const_f32_ptr c1,
-                                                 int nkb, int nrows, int mvalid, v4f (&acc)[2][2][4]) {
-  switch (mvalid) {
-    case 0: tiled_mainloop<BF, 0, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    case 1: tiled_mainloop<BF, 1, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    case 2: tiled_mainloop<BF, 2, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    case 3: tiled_mainloop<BF, 3, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    default: tiled_mainloop<BF, 4, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+template <int ROWS, bool BF, int WPOL>
+__device__ __forceinline__ void run_mainloop_pol(uint8_t* smem, const TileSrc<ROWS>& src, const_f32_ptr c0,
+                                                 const_f32_ptr c1, int nkb, int nrows, int mvalid,
+                                                 v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
+  if constexpr (Tile<ROWS>::MVMAX == 4) {
+    switch (mvalid) {
+      case 0: tiled_mainloop<ROWS, BF, 0, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 1: tiled_mainloop<ROWS, BF, 1, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 2: tiled_mainloop<ROWS, BF, 2, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 3: tiled_mainloop<ROWS, BF, 3, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      default: tiled_mainloop<ROWS, BF, 4, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    }
+  } else {
+    switch (mvalid) {
+      case 0: tiled_mainloop<ROWS, BF, 0, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 1: tiled_mainloop<ROWS, BF, 1, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      default: tiled_mainloop<ROWS, BF, 2, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+    }
   }
 }
 
 // The main loop for this tile (mvalid: wave-uniform count of this wave's
 // 16-row sub-tiles that hold rows), with non-temporal weight copies when the
 // tile reads them once.
-template <bool BF>
-__device__ __forceinline__ void run_mainloop(uint8_t* smem, const TileSrc& src, const float* sa0, const float* sa1,
-                                             int nkb, int nrows, int mvalid, bool once, v4f (&acc)[2][2][4]) {
+template <int ROWS, bool BF>
+__device__ __forceinline__ void run_mainloop(uint8_t* smem, const TileSrc<ROWS>& src, const float* sa0,
+                                             const float* sa1, int nkb, int nrows, int mvalid, bool once,
+                                             v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
   const const_f32_ptr c0 = (const_f32_ptr)sa0, c1 = (const_f32_ptr)sa1;
   if (once)
-    run_mainloop_pol<BF, CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
+    run_mainloop_pol<ROWS, BF, CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
   else
-    run_mainloop_pol<BF, 0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
+    run_mainloop_pol<ROWS, BF, 0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
 }
 
 // DMA source pointers of this lane.  wrow(i): weight row of tile row i
 // (0..255); arow(j): activation row pointer of tile row j (0..127);
 // srow(j): its scale row.
-template <typename WRow, typename ARow, typename SRow>
-__device__ __forceinline__ TileSrc make_tile_src(WRow wrow, ARow arow, SRow srow) {
+template <int ROWS, typename WRow, typename ARow, typename SRow>
+__device__ __forceinline__ TileSrc<ROWS> make_tile_src(WRow wrow, ARow arow, SRow srow) {
+  using G = Tile<ROWS>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int slot = lane & 7;
-  TileSrc t;
+  TileSrc<ROWS> t;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (wave * 4 + i) * 8 + (lane >> 3);
     t.a[i] = wrow(row) + 16 * (slot ^ swz(row));
   }
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = (wave * 2 + j) * 8 + (lane >> 3);
+  for (int j = 0; j < G::APW; ++j) {
+    const int row = min((wave * G::APW + j) * 8 + (lane >> 3), ROWS - 1);
     t.b[j] = arow(row) + 16 * (slot ^ swz(row));
   }
-  t.s = srow(min(wave, 1) * 64 + lane);
+  t.s = srow(min(min(wave, G::SWAVES - 1) * 64 + lane, ROWS - 1));
   return t;
 }
 
 // grid = max_tiles * (I/128), block = 512.  BF: bf16 weights and activations
 // (64-element K blocks, no scales, h stored as bf16).
-template <bool BF>
-__global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[TT_SMEM];
+template <int ROWS, bool BF>
+__global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_up_tiled_kernel(FfnArgs a) {
+  using G = Tile<ROWS>;
+  constexpr int MVX = G::MVMAX;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
   constexpr int EB = BF ? 2 : 1;  // bytes per element
   const int nib = a.I / BLK, nkb = a.d * EB / BLK;
   const int tile = blockIdx.x / nib, ib = blockIdx.x - tile * nib;
@@ -358,7 +406,7 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
   const int wr = wave >> 2, wc = wave & 3;
 
   const int* rt = a.row_token;
-  const TileSrc src = make_tile_src(
+  const TileSrc<ROWS> src = make_tile_src<ROWS>(
       [&](int row) {  // 0..127: w1 rows of block ib, 128..255: w3 rows
         const uint8_t* base = row < 128 ? P.w1 : P.w3;
         return base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d * EB;
@@ -373,20 +421,20 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
         return a.xs + (size_t)tok * nkb;
       });
   const float* sa[2] = {BF ? nullptr : P.s1 + (eo * nib + ib) * nkb, BF ? nullptr : P.s3 + (eo * nib + ib) * nkb};
-  const int mvalid = __builtin_amdgcn_readfirstlane(min(4, max(0, (nrows - wr * 64 + 15) >> 4)));
-  v4f acc[2][2][4];
+  const int mvalid = __builtin_amdgcn_readfirstlane(min(MVX, max(0, (nrows - wr * 64 + 15) >> 4)));
+  v4f acc[2][2][MVX];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop<BF>(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
+      for (int m = 0; m < MVX; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
+  run_mainloop<ROWS, BF>(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
 
   if constexpr (BF) {
     // h = bf16(silu(bf16 g) * bf16 u), stored as bf16
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < MVX; ++m) {
       const int rr = wr * 64 + 16 * m + r;
       if (rr < nrows) {
         const size_t row = (size_t)(row0 + rr);
@@ -412,9 +460,9 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
   // epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32 columns x 64
   // rows; per-row amax over the block's 128 columns (4 waves) via LDS
   float* red = (float*)smem;  // [2][4][64], staging buffers are no longer read
-  float hv[2][4][4];
+  float hv[2][MVX][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MVX; ++m) {
     float amax = 0.f;
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
@@ -432,7 +480,7 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
   }
   __syncthreads();
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MVX; ++m) {
     const int rr = wr * 64 + 16 * m + r;
     if (rr < nrows) {
       float amax = 0.f;
@@ -450,9 +498,11 @@ __global__ __launch_bounds__(512, 1) void ffn_up_tiled_kernel(FfnArgs a) {
 }
 
 // grid = max_tiles * ceil(d/256), block = 512.  BF: bf16 weights and h.
-template <bool BF>
-__global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[TT_SMEM];
+template <int ROWS, bool BF>
+__global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_down_tiled_kernel(FfnArgs a) {
+  using G = Tile<ROWS>;
+  constexpr int MVX = G::MVMAX;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
   constexpr int EB = BF ? 2 : 1;  // bytes per element
   const int nob = a.d / BLK, nkb = a.I * EB / BLK;
   const int nob2 = (nob + 1) >> 1;
@@ -467,7 +517,7 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
   const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
 
-  const TileSrc src = make_tile_src(
+  const TileSrc<ROWS> src = make_tile_src<ROWS>(
       [&](int row) {  // a ragged last pair of blocks reads a valid row
         const int o = min(ob * 256 + row, a.d - 1);
         return P.w2 + (eo * a.d + o) * (size_t)a.I * EB;
@@ -478,18 +528,18 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
       });
   const float* sa[2] = {BF ? nullptr : P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb,
                         BF ? nullptr : P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb};
-  const int mvalid = __builtin_amdgcn_readfirstlane(min(4, max(0, (nrows - wr * 64 + 15) >> 4)));
-  v4f acc[2][2][4];
+  const int mvalid = __builtin_amdgcn_readfirstlane(min(MVX, max(0, (nrows - wr * 64 + 15) >> 4)));
+  v4f acc[2][2][MVX];
 #pragma unroll
   for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop<BF>(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
+      for (int m = 0; m < MVX; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
+  run_mainloop<ROWS, BF>(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
 
 #pragma unroll
-  for (int m = 0; m < 4; ++m) {
+  for (int m = 0; m < MVX; ++m) {
     const int rr = wr * 64 + 16 * m + r;
     if (rr < nrows) {
       const size_t row = (size_t)(row0 + rr);
@@ -510,16 +560,16 @@ __global__ __launch_bounds__(512, 1) void ffn_down_tiled_kernel(FfnArgs a) {
   }
 }
 
-template <bool BF>
+template <int ROWS, bool BF>
 hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
   const int64_t g1 = max_tiles * (a.I / BLK);
   const int64_t g2 = max_tiles * ((a.d / BLK + 1) / 2);
   if (ev) (void)hipEventRecord(ev[0], s);
-  hipLaunchKernelGGL(ffn_up_tiled_kernel<BF>, dim3((unsigned)g1), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((ffn_up_tiled_kernel<ROWS, BF>), dim3((unsigned)g1), dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev) (void)hipEventRecord(ev[1], s);
-  hipLaunchKernelGGL(ffn_down_tiled_kernel<BF>, dim3((unsigned)g2), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((ffn_down_tiled_kernel<ROWS, BF>), dim3((unsigned)g2), dim3(512), 0, s, a);
   err = hipGetLastError();
   if (ev) (void)hipEventRecord(ev[2], s);
   return err;
@@ -527,7 +577,11 @@ hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipE
 
 }  // namespace
 
-int ffn_tile_rows(int64_t) { return TT_ROWS; }
+int ffn_tile_rows(int64_t T) {
+  // small batches: experts hold a few rows each and the weights are the
+  // traffic; narrow tiles let two workgroups share a CU
+  return T <= 128 ? 32 : 128;
+}
 
 int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows) {
   return (T * K) / tile_rows + E + (T + tile_rows - 1) / tile_rows + 1;
@@ -561,7 +615,8 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
   a.hq = hq;
   a.hs = hs;
   a.out = out;
-  return bf16 ? launch_gemms<true>(a, max_tiles, s, ev) : launch_gemms<false>(a, max_tiles, s, ev);
+  if (NT == 32) return bf16 ? launch_gemms<32, true>(a, max_tiles, s, ev) : launch_gemms<32, false>(a, max_tiles, s, ev);
+  return bf16 ? launch_gemms<128, true>(a, max_tiles, s, ev) : launch_gemms<128, false>(a, max_tiles, s, ev);
 }
 
 }  // namespace moe
