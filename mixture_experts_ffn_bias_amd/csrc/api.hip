@@ -281,13 +281,18 @@ int forward_impl(const moe_dims* dims, const float* gate_w, const float* gate_b,
                                  d.route_scale, at<float>(workspace, L.zpart),
                                  gate_ksplit(tokens, d.d_model, d.n_experts), idx, w, s)));
   if (ev) (void)hipEventRecord(ev[1], s);
+  // small batches: the permutation kernel also writes the FFN tile list
+  const PlanArgs plan{at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles), ffn_tile_rows(tokens), 1,
+                      ffn_plan_cap(tokens, d.topk, d.n_experts, true)};
+  bool planned = false;
   MOE_TRY(hip_status(launch_permute(idx, x, T, d.d_model, d.n_experts, d.topk, at<int32_t>(workspace, L.chunk_cnt),
                                     at<int32_t>(workspace, L.chunk_off), at<int32_t>(workspace, L.counts), offsets,
-                                    row_token, pair_row, xq, xs, s)));
+                                    row_token, pair_row, xq, xs, s, &plan, &planned)));
   MOE_TRY(hip_status(launch_ffn(routed, &shared, T, d.d_model, d.inter, d.n_experts, d.topk, offsets, row_token,
                                 bf16 ? (const uint8_t*)x : xq, xs, at<int4>(workspace, L.tiles),
                                 at<int32_t>(workspace, L.n_tiles), at<uint8_t>(workspace, L.hq),
-                                bf16 ? nullptr : at<float>(workspace, L.hs), rows, s, ev ? ev + 2 : nullptr, bf16)));
+                                bf16 ? nullptr : at<float>(workspace, L.hs), rows, s, ev ? ev + 2 : nullptr, bf16, 0,
+                                -1, planned)));
   const int st = hip_status(launch_combine(idx, w, pair_row, rows, 1, T, d.topk, d.n_experts, d.d_model, delta, s));
   if (ev) (void)hipEventRecord(ev[5], s);
   return st;

@@ -16,6 +16,7 @@
 // (16 rows); lane l ends with features 4*(l/16)+j of row l%16.
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -28,41 +29,22 @@ __device__ __forceinline__ int token_of(const int32_t* row_token, int row, int T
   return row_token ? clampi(row_token[row], 0, T - 1) : row;
 }
 
-// One block of 256 threads.  tiles[i] = {expert, first row, rows, once} for
-// the routed experts [e_lo, e_hi) (expert numbered from e_lo) and, with
-// has_shared, the shared expert, numbered e_hi - e_lo, with rows
-// [T*K, T*K + T).  once = 1 when the tile is the only one of its expert, so
-// its weights are read exactly once.  The shared expert's tiles come first:
-// they hold the most rows when T is small, and starting the longest work
-// first keeps it off the end of the launch.
+// One block of 256 threads: the tile list from the expert offsets
+// (plan_tiles_block).  The shared expert's tiles come first: they hold the
+// most rows when T is small, and starting the longest work first keeps it
+// off the end of the launch.
 __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restrict__ offsets, int e_lo, int e_hi,
                                                          int T, int K, int NT, int has_shared, int cap,
                                                          int4* __restrict__ tiles, int32_t* __restrict__ n_tiles) {
   __shared__ int s[256];
   const int e = threadIdx.x;
   const int TK = T * K;
-  const int nsh = has_shared ? (T + NT - 1) / NT : 0;
-  for (int j = threadIdx.x; j < nsh; j += blockDim.x)
-    tiles[j] = make_int4(e_hi - e_lo, TK + j * NT, min(NT, T - j * NT), nsh == 1 ? 1 : 0);
-  int lo = 0, cnt = 0, n = 0;
+  int lo = 0, cnt = 0;
   if (e >= e_lo && e < e_hi) {
     lo = clampi(offsets[e], 0, TK);
-    const int hi = clampi(offsets[e + 1], lo, TK);
-    cnt = hi - lo;
-    n = (cnt + NT - 1) / NT;
+    cnt = clampi(offsets[e + 1], lo, TK) - lo;
   }
-  s[e] = n;
-  __syncthreads();
-  for (int o = 1; o < 256; o <<= 1) {
-    const int v = e >= o ? s[e - o] : 0;
-    __syncthreads();
-    s[e] += v;
-    __syncthreads();
-  }
-  const int base = s[e] - n;
-  for (int j = 0; j < n && base + j < cap; ++j)
-    tiles[nsh + base + j] = make_int4(e - e_lo, lo + j * NT, min(NT, cnt - j * NT), n == 1 ? 1 : 0);
-  if (threadIdx.x == 0) *n_tiles = nsh + min(s[255], cap);
+  plan_tiles_block(lo, cnt, T, K, NT, has_shared, cap, e_lo, e_hi, s, tiles, n_tiles);
 }
 
 // With e4m3 weights, xq/hq are e4m3 rows with block scales xs/hs; with bf16
@@ -587,18 +569,25 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows) {
   return (T * K) / tile_rows + E + (T + tile_rows - 1) / tile_rows + 1;
 }
 
+int ffn_plan_cap(int64_t T, int K, int E, bool has_shared) {
+  const int NT = ffn_tile_rows(T);
+  return (int)(ffn_max_tiles(T, K, E, NT) - (has_shared ? (T + NT - 1) / NT : 0));
+}
+
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E, int K,
                       const int32_t* offsets, const int32_t* row_token, const uint8_t* xq, const float* xs,
                       int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs, uint16_t* out, hipStream_t s,
-                      hipEvent_t* ev, bool bf16, int e_lo, int e_hi) {
+                      hipEvent_t* ev, bool bf16, int e_lo, int e_hi, bool planned) {
   if (e_hi < 0) e_hi = E;
   const int NT = ffn_tile_rows(T);
   const int64_t max_tiles = ffn_max_tiles(T, K, E, NT);
   const int nsh = shared ? (T + NT - 1) / NT : 0;
-  hipLaunchKernelGGL(plan_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, e_lo, e_hi, T, K, NT, shared ? 1 : 0,
-                     (int)(max_tiles - nsh), tiles, n_tiles);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (!planned) {
+    hipLaunchKernelGGL(plan_tiles_kernel, dim3(1), dim3(256), 0, s, offsets, e_lo, e_hi, T, K, NT, shared ? 1 : 0,
+                       (int)(max_tiles - nsh), tiles, n_tiles);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   FfnArgs a;
   a.routed = routed;
   a.shared = shared ? *shared : routed;

@@ -26,9 +26,21 @@ hipError_t launch_gate(const uint16_t* x, const float* gate_w, const float* gate
                        float* w, hipStream_t s);
 
 // permute.hip
+// The FFN tile list for all E experts, written alongside the permutation
+// when the batch fits one permutation chunk (see launch_ffn).
+struct PlanArgs {
+  int4* tiles;
+  int32_t* n_tiles;
+  int tile_rows;
+  int has_shared;
+  int cap;
+};
+// plan (may be NULL): also write the tile list when T <= PERM_CHUNK; *planned
+// (may be NULL) tells whether it was written.
 hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, int E, int K,
                           int32_t* chunk_cnt, int32_t* chunk_off, int32_t* counts, int32_t* offsets,
-                          int32_t* row_token, int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s);
+                          int32_t* row_token, int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s,
+                          const PlanArgs* plan = nullptr, bool* planned = nullptr);
 // per-128-block e4m3 quantisation of T rows of d bf16 values
 hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s);
 
@@ -44,12 +56,15 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
 // are unused.
 // [e_lo, e_hi) (e_hi < 0: E): the routed experts to run; `routed` then holds
 // exactly those experts (expert e_lo first).  Rows of other experts are left
-// untouched.
+// untouched.  planned: the tile list is already in tiles / n_tiles (written
+// by launch_permute with a PlanArgs), so no plan kernel runs.
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E,
                       int K, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
                       const float* xs, int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs,
                       uint16_t* out, hipStream_t s, hipEvent_t* ev = nullptr, bool bf16 = false,
-                      int e_lo = 0, int e_hi = -1);
+                      int e_lo = 0, int e_hi = -1, bool planned = false);
+// routed tiles the plan may write (the tile list holds ffn_max_tiles entries)
+int ffn_plan_cap(int64_t T, int K, int E, bool has_shared);
 
 // combine.hip
 hipError_t launch_combine(const int32_t* idx, const float* w, const int32_t* pair_row, const uint16_t* rows,

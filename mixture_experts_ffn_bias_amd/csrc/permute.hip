@@ -11,6 +11,7 @@
 // its final row directly and the order is deterministic.
 #include "common.h"
 #include "kernels.h"
+#include "plan.h"
 
 namespace moe {
 
@@ -141,7 +142,8 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 __global__ __launch_bounds__(PERM_CHUNK) void permute_small_kernel(
     const int32_t* __restrict__ idx, int T, int K, int E, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ row_token, int32_t* __restrict__ pair_row,
-    const uint16_t* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ q, float* __restrict__ scale) {
+    const uint16_t* __restrict__ x, int64_t nblocks, uint8_t* __restrict__ q, float* __restrict__ scale,
+    PlanArgs plan) {
   if (blockIdx.x > 0) {
     const int64_t gid = (int64_t)(blockIdx.x - 1) * blockDim.x + threadIdx.x;
     const int64_t blk = gid >> 3;
@@ -188,6 +190,11 @@ __global__ __launch_bounds__(PERM_CHUNK) void permute_small_kernel(
     }
     row_token[(size_t)T * K + t] = t;
   }
+  if (plan.tiles) {  // the FFN tile list from the same offsets
+    __syncthreads();  // s is reused as the plan's scan buffer
+    plan_tiles_block(e < E ? s_off[e] : 0, e < E ? cnt : 0, T, K, plan.tile_rows, plan.has_shared, plan.cap, 0, E, s,
+                     plan.tiles, plan.n_tiles);
+  }
 }
 
 }  // namespace
@@ -201,13 +208,17 @@ hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float*
 
 hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, int E, int K, int32_t* chunk_cnt,
                           int32_t* chunk_off, int32_t* counts, int32_t* offsets, int32_t* row_token,
-                          int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s) {
+                          int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s, const PlanArgs* plan,
+                          bool* planned) {
   const int nchunks = (T + PERM_CHUNK - 1) / PERM_CHUNK;
+  if (planned) *planned = false;
   if (nchunks == 1) {
+    const PlanArgs pa = plan ? *plan : PlanArgs{nullptr, nullptr, 0, 0, 0};
     const int64_t nblocks = xq ? (int64_t)T * (d / BLK) : 0;  // no quantisation without xq
     const int64_t qblocks = (nblocks * 8 + PERM_CHUNK - 1) / PERM_CHUNK;
     hipLaunchKernelGGL(permute_small_kernel, dim3((unsigned)(1 + qblocks)), dim3(PERM_CHUNK), 0, s, idx, T, K, E,
-                       counts, offsets, row_token, pair_row, x, nblocks, xq, xs);
+                       counts, offsets, row_token, pair_row, x, nblocks, xq, xs, pa);
+    if (planned) *planned = plan != nullptr;
     return hipGetLastError();
   }
   hipLaunchKernelGGL(count_kernel, dim3(nchunks), dim3(PERM_CHUNK), 0, s, idx, T, K, E, chunk_cnt);
