@@ -209,6 +209,72 @@ __device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
   return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
 
+// One K block of the tile: this wave's block products from the stage buffer
+// `stage`, scaled and added to acc (MV: the wave's 16-row sub-tiles that hold
+// rows; 0 multiplies nothing).
+template <int ROWS, bool BF, int MV>
+__device__ __forceinline__ void kblock_multiply(const uint8_t* stage, const_f32_ptr sa0, const_f32_ptr sa1, int kb,
+                                                v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
+  using G = Tile<ROWS>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int wr = wave >> 2, wc = wave & 3;
+  if constexpr (BF && MV > 0) {
+    // bf16 operands: the 128 bytes of a row are 64 k values, two MFMAs per block, no scales
+    const uint8_t* la = stage;
+    const uint8_t* lb = la + TT_A_BYTES;
+    FragH B[MV];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) B[m] = as_bf16(lds_frag(lb, wr * 64 + 16 * m + r, g));
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const FragH A = as_bf16(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+          for (int m = 0; m < MV; ++m)
+            acc[gi][jt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], acc[gi][jt][m], 0, 0, 0);
+      }
+    }
+  }
+  if constexpr (!BF && MV > 0) {
+    const uint8_t* la = stage;
+    const uint8_t* lb = la + TT_A_BYTES;
+    const float* ls = (const float*)(lb + G::B_BYTES);
+    const float s_a0 = sa0[kb], s_a1 = sa1[kb];
+    Frag B[MV];
+    float sb[MV];
+#pragma unroll
+    for (int m = 0; m < MV; ++m) {
+      B[m] = decode_e4m3(lds_frag(lb, wr * 64 + 16 * m + r, g));
+      sb[m] = ls[wr * 64 + 16 * m + r];
+    }
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        const Frag A = decode_e4m3(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
+        const float sg = gi == 0 ? s_a0 : s_a1;
+        // MV independent accumulation chains, issued round-robin
+        v4f p[MV];
+#pragma unroll
+        for (int m = 0; m < MV; ++m) p[m] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int m = 0; m < MV; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], p[m], 0, 0, 0);
+#pragma unroll
+        for (int m = 0; m < MV; ++m) {
+          const float f = sg * sb[m];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[m][j], f, acc[gi][jt][m][j]);
+        }
+      }
+    }
+  }
+}
+
 // Main loop shared by both projections.  src: this lane's DMA sources.
 // sa0, sa1: weight block scales of the two weight groups over K.
 // acc[gi][jt][m].  MV: the 16-row sub-tiles of this wave that hold rows
@@ -248,61 +314,7 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS
       tile_issue<ROWS, BF, WPOL>(src, smem + nb * G::STAGE, kb + AHEAD, wave, act);
     }
     // a wave whose 64 rows hold no tile row (MV = 0) only helps with the copies
-    if constexpr (BF && MV > 0) {
-      // bf16 operands: the 128 bytes of a row are 64 k values, two MFMAs per block, no scales
-      const uint8_t* la = smem + cur * G::STAGE;
-      const uint8_t* lb = la + TT_A_BYTES;
-      FragH B[MV];
-#pragma unroll
-      for (int m = 0; m < MV; ++m) B[m] = as_bf16(lds_frag(lb, wr * 64 + 16 * m + r, g));
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const FragH A = as_bf16(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
-#pragma unroll
-          for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int m = 0; m < MV; ++m)
-              acc[gi][jt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], acc[gi][jt][m], 0, 0, 0);
-        }
-      }
-    }
-    if constexpr (!BF && MV > 0) {
-      const uint8_t* la = smem + cur * G::STAGE;
-      const uint8_t* lb = la + TT_A_BYTES;
-      const float* ls = (const float*)(lb + G::B_BYTES);
-      const float s_a0 = sa0[kb], s_a1 = sa1[kb];
-      Frag B[MV];
-      float sb[MV];
-#pragma unroll
-      for (int m = 0; m < MV; ++m) {
-        B[m] = decode_e4m3(lds_frag(lb, wr * 64 + 16 * m + r, g));
-        sb[m] = ls[wr * 64 + 16 * m + r];
-      }
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          const Frag A = decode_e4m3(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
-          const float sg = gi == 0 ? s_a0 : s_a1;
-          // MV independent accumulation chains, issued round-robin
-          v4f p[MV];
-#pragma unroll
-          for (int m = 0; m < MV; ++m) p[m] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int m = 0; m < MV; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], p[m], 0, 0, 0);
-#pragma unroll
-          for (int m = 0; m < MV; ++m) {
-            const float f = sg * sb[m];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[m][j], f, acc[gi][jt][m][j]);
-          }
-        }
-      }
-    }
+    kblock_multiply<ROWS, BF, MV>(smem + cur * G::STAGE, sa0, sa1, kb, acc);
     if (kb + 1 < nkb) wait_vmcnt_upto(per_stage * (min(kb + AHEAD, nkb - 1) - kb - 1));
     pipeline_barrier();
     cur = cur == G::NSTAGE - 1 ? 0 : cur + 1;
@@ -367,28 +379,43 @@ __device__ __forceinline__ TileSrc<ROWS> make_tile_src(WRow wrow, ARow arow, SRo
   return t;
 }
 
-// grid = max_tiles * (I/128), block = 512.  BF: bf16 weights and activations
-// (64-element K blocks, no scales, h stored as bf16).
+// LDS exchange barrier: this wave's LDS stores are complete (lgkmcnt) and
+// every wave has arrived.  Unlike __syncthreads it does not wait for the
+// wave's global -> LDS copies, which may still be in flight for the next
+// K block.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// One work item of a projection: a tile and a block of output columns.
+template <int ROWS>
+struct Item {
+  TileSrc<ROWS> src;   // this lane's copy sources
+  const float* sa0;    // weight block scales of the two weight groups over K (e4m3)
+  const float* sa1;
+  int blk;             // up: the 128-wide h block; down: the pair of 128-feature output blocks
+  int row0, nrows;     // the tile's permuted rows
+  bool once;           // the tile is the only one of its expert
+};
+
+// Item `item` of the up-projection (tile item / nib, h block item % nib);
+// false past the last tile.
 template <int ROWS, bool BF>
-__global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_up_tiled_kernel(FfnArgs a) {
-  using G = Tile<ROWS>;
-  constexpr int MVX = G::MVMAX;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
-  constexpr int EB = BF ? 2 : 1;  // bytes per element
+__device__ __forceinline__ bool up_item(const FfnArgs& a, int item, Item<ROWS>& it) {
+  constexpr int EB = BF ? 2 : 1;
   const int nib = a.I / BLK, nkb = a.d * EB / BLK;
-  const int tile = blockIdx.x / nib, ib = blockIdx.x - tile * nib;
-  if (tile >= *a.n_tiles) return;  // uniform for the whole block, before any barrier
+  const int tile = item / nib, ib = item - tile * nib;
+  if (tile >= *a.n_tiles) return false;
   const int4 td = a.tiles[tile];
   const int e = td.x, row0 = td.y, nrows = td.z;
   const bool sh = e >= a.E;
   const ExpertPtrs& P = sh ? a.shared : a.routed;
   const size_t eo = sh ? 0 : (size_t)e;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
-  const int wr = wave >> 2, wc = wave & 3;
-
   const int* rt = a.row_token;
-  const TileSrc<ROWS> src = make_tile_src<ROWS>(
+  it.src = make_tile_src<ROWS>(
       [&](int row) {  // 0..127: w1 rows of block ib, 128..255: w3 rows
         const uint8_t* base = row < 128 ? P.w1 : P.w3;
         return base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d * EB;
@@ -402,24 +429,71 @@ __global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_up_tiled_kernel(
         const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T);
         return a.xs + (size_t)tok * nkb;
       });
-  const float* sa[2] = {BF ? nullptr : P.s1 + (eo * nib + ib) * nkb, BF ? nullptr : P.s3 + (eo * nib + ib) * nkb};
-  const int mvalid = __builtin_amdgcn_readfirstlane(min(MVX, max(0, (nrows - wr * 64 + 15) >> 4)));
-  v4f acc[2][2][MVX];
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int m = 0; m < MVX; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop<ROWS, BF>(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
+  it.sa0 = BF ? nullptr : P.s1 + (eo * nib + ib) * nkb;
+  it.sa1 = BF ? nullptr : P.s3 + (eo * nib + ib) * nkb;
+  it.blk = ib;
+  it.row0 = row0;
+  it.nrows = nrows;
+  it.once = td.w != 0;
+  return true;
+}
 
+// Item `item` of the down-projection (tile item / nob2, output blocks
+// 2 (item % nob2) and 2 (item % nob2) + 1); false past the last tile.
+template <int ROWS, bool BF>
+__device__ __forceinline__ bool down_item(const FfnArgs& a, int item, Item<ROWS>& it) {
+  constexpr int EB = BF ? 2 : 1;
+  const int nob = a.d / BLK, nkb = a.I * EB / BLK;
+  const int nob2 = (nob + 1) >> 1;
+  const int tile = item / nob2, ob = item - tile * nob2;
+  if (tile >= *a.n_tiles) return false;
+  const int4 td = a.tiles[tile];
+  const int e = td.x, row0 = td.y, nrows = td.z;
+  const bool sh = e >= a.E;
+  const ExpertPtrs& P = sh ? a.shared : a.routed;
+  const size_t eo = sh ? 0 : (size_t)e;
+  it.src = make_tile_src<ROWS>(
+      [&](int row) {  // a ragged last pair of blocks reads a valid row
+        const int o = min(ob * 256 + row, a.d - 1);
+        return P.w2 + (eo * a.d + o) * (size_t)a.I * EB;
+      },
+      [&](int row) { return a.hq + (size_t)(row0 + min(row, nrows - 1)) * a.I * EB; },
+      [&](int row) -> const float* {
+        return BF ? nullptr : a.hs + (size_t)(row0 + min(row, nrows - 1)) * nkb;
+      });
+  it.sa0 = BF ? nullptr : P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb;
+  it.sa1 = BF ? nullptr : P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb;
+  it.blk = ob;
+  it.row0 = row0;
+  it.nrows = nrows;
+  it.once = td.w != 0;
+  return true;
+}
+
+// 16-row sub-tiles of this wave that hold rows of the item (wave-uniform)
+template <int ROWS>
+__device__ __forceinline__ int item_mvalid(const Item<ROWS>& it) {
+  const int wr = (threadIdx.x >> 6) >> 2;
+  return __builtin_amdgcn_readfirstlane(min(Tile<ROWS>::MVMAX, max(0, (it.nrows - wr * 64 + 15) >> 4)));
+}
+
+// Up-projection epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32
+// columns of h block it.blk x its 64 rows; e4m3: per-row amax over the
+// block's 128 columns (4 waves) through `red` (2 KiB of LDS), then e4m3 h
+// and its scale; bf16: h itself.
+template <int ROWS, bool BF>
+__device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& it,
+                                            const v4f (&acc)[2][2][Tile<ROWS>::MVMAX], float* red) {
+  constexpr int MVX = Tile<ROWS>::MVMAX;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const int wr = wave >> 2, wc = wave & 3;
+  const int nib = a.I / BLK;
   if constexpr (BF) {
-    // h = bf16(silu(bf16 g) * bf16 u), stored as bf16
 #pragma unroll
     for (int m = 0; m < MVX; ++m) {
       const int rr = wr * 64 + 16 * m + r;
-      if (rr < nrows) {
-        const size_t row = (size_t)(row0 + rr);
+      if (rr < it.nrows) {
+        const size_t row = (size_t)(it.row0 + rr);
 #pragma unroll
         for (int jt = 0; jt < 2; ++jt) {
           uint16_t hb[4];
@@ -432,16 +506,12 @@ __global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_up_tiled_kernel(
           uint2 o;
           o.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
           o.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
-          *(uint2*)((uint16_t*)a.hq + row * a.I + ib * BLK + wc * 32 + jt * 16 + 4 * g) = o;
+          *(uint2*)((uint16_t*)a.hq + row * a.I + it.blk * BLK + wc * 32 + jt * 16 + 4 * g) = o;
         }
       }
     }
     return;
   }
-
-  // epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32 columns x 64
-  // rows; per-row amax over the block's 128 columns (4 waves) via LDS
-  float* red = (float*)smem;  // [2][4][64], staging buffers are no longer read
   float hv[2][MVX][4];
 #pragma unroll
   for (int m = 0; m < MVX; ++m) {
@@ -460,81 +530,49 @@ __global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_up_tiled_kernel(
     amax = fmaxf(amax, __shfl_xor(amax, 32));
     if (g == 0) red[(wr * 4 + wc) * 64 + 16 * m + r] = amax;
   }
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int m = 0; m < MVX; ++m) {
     const int rr = wr * 64 + 16 * m + r;
-    if (rr < nrows) {
+    if (rr < it.nrows) {
       float amax = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) amax = fmaxf(amax, red[(wr * 4 + c) * 64 + 16 * m + r]);
       const float sc = amax == 0.f ? 1.f : amax / E4M3_MAX;
-      const size_t row = (size_t)(row0 + rr);
+      const size_t row = (size_t)(it.row0 + rr);
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
-        *(uint32_t*)(a.hq + row * a.I + ib * BLK + wc * 32 + jt * 16 + 4 * g) =
+        *(uint32_t*)(a.hq + row * a.I + it.blk * BLK + wc * 32 + jt * 16 + 4 * g) =
             pack4_e4m3(hv[jt][m][0] / sc, hv[jt][m][1] / sc, hv[jt][m][2] / sc, hv[jt][m][3] / sc);
-      if (wc == 0 && g == 0) a.hs[row * nib + ib] = sc;
+      if (wc == 0 && g == 0) a.hs[row * nib + it.blk] = sc;
     }
   }
 }
 
-// grid = max_tiles * ceil(d/256), block = 512.  BF: bf16 weights and h.
-template <int ROWS, bool BF>
-__global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_down_tiled_kernel(FfnArgs a) {
-  using G = Tile<ROWS>;
-  constexpr int MVX = G::MVMAX;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
-  constexpr int EB = BF ? 2 : 1;  // bytes per element
-  const int nob = a.d / BLK, nkb = a.I * EB / BLK;
-  const int nob2 = (nob + 1) >> 1;
-  const int tile = blockIdx.x / nob2, ob = blockIdx.x - tile * nob2;
-  if (tile >= *a.n_tiles) return;
-  const int4 td = a.tiles[tile];
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const bool sh = e >= a.E;
-  const ExpertPtrs& P = sh ? a.shared : a.routed;
-  const size_t eo = sh ? 0 : (size_t)e;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63, r = lane & 15, g = lane >> 4;
+// Down-projection epilogue: the wave's rows of output blocks 2 it.blk and
+// 2 it.blk + 1 (the second may lie past d), bf16.
+template <int ROWS>
+__device__ __forceinline__ void down_epilogue(const FfnArgs& a, const Item<ROWS>& it,
+                                              const v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
+  constexpr int MVX = Tile<ROWS>::MVMAX;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
-
-  const TileSrc<ROWS> src = make_tile_src<ROWS>(
-      [&](int row) {  // a ragged last pair of blocks reads a valid row
-        const int o = min(ob * 256 + row, a.d - 1);
-        return P.w2 + (eo * a.d + o) * (size_t)a.I * EB;
-      },
-      [&](int row) { return a.hq + (size_t)(row0 + min(row, nrows - 1)) * a.I * EB; },
-      [&](int row) -> const float* {
-        return BF ? nullptr : a.hs + (size_t)(row0 + min(row, nrows - 1)) * nkb;
-      });
-  const float* sa[2] = {BF ? nullptr : P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb,
-                        BF ? nullptr : P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb};
-  const int mvalid = __builtin_amdgcn_readfirstlane(min(MVX, max(0, (nrows - wr * 64 + 15) >> 4)));
-  v4f acc[2][2][MVX];
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int m = 0; m < MVX; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-  run_mainloop<ROWS, BF>(smem, src, sa[0], sa[1], nkb, nrows, mvalid, td.w != 0, acc);
-
+  const int nob = a.d / BLK;
 #pragma unroll
   for (int m = 0; m < MVX; ++m) {
     const int rr = wr * 64 + 16 * m + r;
-    if (rr < nrows) {
-      const size_t row = (size_t)(row0 + rr);
+    if (rr < it.nrows) {
+      const size_t row = (size_t)(it.row0 + rr);
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
-        if (2 * ob + gi < nob) {
+        if (2 * it.blk + gi < nob) {
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
             const v4f v = acc[gi][jt][m];
             uint2 o;
             o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
             o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-            *(uint2*)(a.out + row * a.d + (2 * ob + gi) * BLK + wc * 32 + jt * 16 + 4 * g) = o;
+            *(uint2*)(a.out + row * a.d + (2 * it.blk + gi) * BLK + wc * 32 + jt * 16 + 4 * g) = o;
           }
         }
       }
@@ -542,16 +580,47 @@ __global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_down_tiled_kerne
   }
 }
 
+template <int ROWS>
+__device__ __forceinline__ void zero_acc(v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
+#pragma unroll
+  for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int m = 0; m < Tile<ROWS>::MVMAX; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
+}
+
+// One item per workgroup.  UP: grid = max_tiles * (I/128); down: grid =
+// max_tiles * ceil(d/256).  Block = 512.  BF: bf16 weights and activations
+// (64-element K blocks, no scales, h stored as bf16).
+template <bool UP, int ROWS, bool BF>
+__global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_tiled_kernel(FfnArgs a) {
+  using G = Tile<ROWS>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
+  constexpr int EB = BF ? 2 : 1;
+  const int nkb = (UP ? a.d : a.I) * EB / BLK;
+  Item<ROWS> it;
+  if (!(UP ? up_item<ROWS, BF>(a, blockIdx.x, it) : down_item<ROWS, BF>(a, blockIdx.x, it)))
+    return;  // uniform for the whole block, before any barrier
+  v4f acc[2][2][G::MVMAX];
+  zero_acc<ROWS>(acc);
+  run_mainloop<ROWS, BF>(smem, it.src, it.sa0, it.sa1, nkb, it.nrows, item_mvalid(it), it.once, acc);
+  if constexpr (UP)
+    up_epilogue<ROWS, BF>(a, it, acc, (float*)smem);  // the stage buffers are no longer read
+  else
+    down_epilogue<ROWS>(a, it, acc);
+}
+
 template <int ROWS, bool BF>
 hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
   const int64_t g1 = max_tiles * (a.I / BLK);
   const int64_t g2 = max_tiles * ((a.d / BLK + 1) / 2);
   if (ev) (void)hipEventRecord(ev[0], s);
-  hipLaunchKernelGGL((ffn_up_tiled_kernel<ROWS, BF>), dim3((unsigned)g1), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((ffn_tiled_kernel<true, ROWS, BF>), dim3((unsigned)g1), dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (ev) (void)hipEventRecord(ev[1], s);
-  hipLaunchKernelGGL((ffn_down_tiled_kernel<ROWS, BF>), dim3((unsigned)g2), dim3(512), 0, s, a);
+  hipLaunchKernelGGL((ffn_tiled_kernel<false, ROWS, BF>), dim3((unsigned)g2), dim3(512), 0, s, a);
   err = hipGetLastError();
   if (ev) (void)hipEventRecord(ev[2], s);
   return err;
