@@ -219,6 +219,9 @@ def main():
     ap.add_argument("--ep-share", type=int, default=0, metavar="N",
                     help="time one rank's share of an N-way expert-parallel layer instead: experts [0, E/N) "
                          "plus the shared expert over all tokens (moe_forward_shard, fp32 partial output)")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the single-launch forward (moe_forward_fused: one kernel for the whole layer, "
+                         "at most 64 tokens, e4m3 weights) instead of the per-step kernels")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -249,6 +252,8 @@ def main():
         return
     if args.ep_share:
         return bench_share(args, moe, synth, torch, np, dev)
+    if args.fused:
+        return bench_fused(args, moe, synth, torch, np, dev)
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
     bf16 = args.weights == "bf16"
@@ -440,6 +445,64 @@ def bench_share(args, moe, synth, torch, np, dev):
         "roofline": roof, "cpu_baseline": None,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_fused(args, moe, synth, torch, np, dev):
+    """The whole layer as one kernel launch (moe_forward_fused), timed launch by launch."""
+    wl = synth.WORKLOADS[args.workload]
+    dims = wl.dims
+    if wl.blocks != 1 or args.weights != "e4m3":
+        sys.exit("--fused takes a single-block workload and e4m3 weights")
+    data = synth.make_workload(args.workload, device=dev)
+    T = data["tokens"]
+    if T > moe.FUSED_MAX_TOKENS:
+        sys.exit(f"--fused runs at most {moe.FUSED_MAX_TOKENS} tokens (workload has {T})")
+    cd = moe.make_dims(dims.d_model, dims.n_experts, dims.n_groups, dims.topk_groups, dims.topk, dims.inter,
+                       dims.route_scale)
+    layer = moe.MoELayer(cd, data["blocks"][0])
+    x = data["x"]
+    ws = moe.fused_workspace(cd, T, device=dev)
+    delta = torch.empty_like(x)
+    idx = torch.empty((T, dims.topk), dtype=torch.int32, device=dev)
+    w = torch.empty((T, dims.topk), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        moe.moe_forward_fused(cd, layer.weights, T, x, delta, idx, w, ws, stream)
+    if moe.moe_forward_fused_status(ws, stream) != 0:
+        sys.exit("moe_forward_fused: a wait gave up (status MOE_ERR_STALLED)")
+    hev = HipEvents()
+    K = args.steps
+    ev = hev.create(2 * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        hev.record(ev[2 * k], stream.cuda_stream)
+        moe.moe_forward_fused(cd, layer.weights, T, x, delta, idx, w, ws, stream)
+        hev.record(ev[2 * k + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(hev.ms(ev[2 * k], ev[2 * k + 1]) for k in range(K)) / K
+    hev.close()
+    status = moe.moe_forward_fused_status(ws, stream)
+    touched = int((np.bincount(idx.cpu().numpy().ravel(), minlength=dims.n_experts) > 0).sum())
+    work = algorithmic_work(dims, T, touched)
+    gbs = work["layer_bytes"] / (launch_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "kernel": "decode_kernel (whole layer, one launch)",
+            "traffic": None, "launch_ms": round(launch_ms, 4), "alg_bytes": int(work["layer_bytes"]),
+            "alg_flops": int(work["layer_flops"])}
+    out = {
+        "metric": "MoE layer tokens/s (d7168,256e,top8) + % of fp8 MFMA / HBM roofline",
+        "value": round(T * K / wall, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "path": "single launch (moe_forward_fused)",
+                   "touched_experts": touched, "status": "ok" if status == 0 else "stalled"},
+        "roofline": roof, "cpu_baseline": None,
+    }
+    print(json.dumps(out), flush=True)
+    if status != 0:
+        sys.exit("moe_forward_fused: a wait gave up during the timed launches")
 
 
 if __name__ == "__main__":

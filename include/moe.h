@@ -13,7 +13,9 @@
  *    comment says "host".  Structs passed by pointer are host memory, read
  *    during the call only.
  *  - The caller owns every buffer.  The library allocates nothing, keeps no
- *    state between calls and never synchronises the host: work is enqueued
+ *    state between calls (moe_forward_fused keeps counters in the caller's
+ *    workspace) and never synchronises the host (moe_forward_fused_status
+ *    does, by design): work is enqueued
  *    on `stream` (a hipStream_t; NULL = the default stream) and a return of
  *    MOE_OK means "enqueued".  Calls on different streams are independent as
  *    long as their buffers (workspace included) do not overlap.
@@ -45,7 +47,8 @@ typedef enum {
   MOE_ERR_UNSUPPORTED = -2, /* dims outside what the kernels implement */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than moe_workspace_size() */
   MOE_ERR_ALIGN = -4,       /* a pointer is not aligned as documented */
-  MOE_ERR_HIP = -5          /* a HIP launch failed */
+  MOE_ERR_HIP = -5,         /* a HIP launch failed */
+  MOE_ERR_STALLED = -6      /* moe_forward_fused_status: a wait inside the last call gave up */
 } moe_status;
 
 /* Layer shape (host struct).  DeepSeek-V3.2-Exp: {7168, 256, 8, 4, 8, 2048, 2.5}. */
@@ -230,6 +233,35 @@ int moe_forward_shard(const moe_dims* dims, const moe_weights* weights, int64_t 
                       int32_t expert_begin, int32_t expert_end, int32_t with_shared,
                       const uint16_t* x, const int32_t* idx, const float* w, float* y_partial,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes moe_forward_fused needs; 0 when the call is not supported
+ * for these dims and tokens (tokens must lie in [1, 64]). */
+size_t moe_forward_fused_workspace_size(const moe_dims* dims, int64_t tokens);
+
+/* moe_forward in ONE kernel launch, for small batches (1 <= tokens <= 64,
+ * e4m3 expert weights): router, permutation, the up- and down-projections of
+ * the routed and shared experts and the combine ("MoE update", moe-forward
+ * excerpt, every step) run as one grid whose workgroups wait on each other's
+ * completion counts in device memory.  Same arguments and the same result as
+ * moe_forward (the router adds its K-split partial logits in a different
+ * grouping, so a logit may differ in its last fp32 bits).
+ * Workspace: moe_forward_fused_workspace_size(dims, tokens) bytes, 256-byte
+ * aligned.  Its first 4096 bytes carry completion counts from call to call:
+ * they must be zero before the first call on a workspace (zero the whole
+ * workspace once), and every completed call leaves them zero except the
+ * status word that moe_forward_fused_status reads.  Calls sharing a
+ * workspace must be ordered (one stream).  A wait that cannot complete gives
+ * up after a bounded time instead of hanging; the call's outputs are then not
+ * valid and moe_forward_fused_status reports MOE_ERR_STALLED. */
+int moe_forward_fused(const moe_dims* dims, const moe_weights* weights, int64_t tokens,
+                      const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Status of the last moe_forward_fused call on `workspace` enqueued on
+ * `stream`: waits for the stream (the one call here that synchronises the
+ * host), then returns MOE_OK or MOE_ERR_STALLED (MOE_ERR_HIP if the wait or
+ * the copy fails). */
+int moe_forward_fused_status(const void* workspace, void* stream);
 
 /* Fused residual add + RMSNorm ("MoE update", rmsnorm excerpt, residual branch):
  *   r = float(x) + float(residual);  residual <- bf16(r);

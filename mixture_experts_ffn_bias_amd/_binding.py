@@ -19,8 +19,10 @@ LIB_PATH = os.path.join(HERE, "libmoe.so")
 MOE_OK = 0
 SYMBOLS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_bf16", "moe_combine",
            "moe_forward", "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_forward_shard",
-           "moe_add_rmsnorm",
+           "moe_forward_fused_workspace_size", "moe_forward_fused", "moe_forward_fused_status", "moe_add_rmsnorm",
            "moe_mlp_workspace_size", "moe_mlp", "moe_status_string")
+MOE_ERR_STALLED = -6
+FUSED_MAX_TOKENS = 64
 MOE_FORWARD_EVENTS = 6
 
 
@@ -82,13 +84,17 @@ def lib() -> ctypes.CDLL:
         L.moe_forward_bf16_timed.argtypes = [dp, ctypes.POINTER(moe_weights_bf16), i64, vp, vp, vp, vp, vp, sz, vp,
                                              ctypes.POINTER(ctypes.c_void_p)]
         L.moe_forward_shard.argtypes = [dp, ctypes.POINTER(moe_weights), i64, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_forward_fused_workspace_size.argtypes = [dp, i64]
+        L.moe_forward_fused_workspace_size.restype = sz
+        L.moe_forward_fused.argtypes = [dp, ctypes.POINTER(moe_weights), i64, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_forward_fused_status.argtypes = [vp, vp]
         L.moe_add_rmsnorm.argtypes = [i32, i64, vp, vp, vp, ctypes.c_float, vp, vp]
         L.moe_mlp_workspace_size.argtypes = [i32, i32, i64]
         L.moe_mlp_workspace_size.restype = sz
         L.moe_mlp.argtypes = [i32, i32, i64, ctypes.POINTER(moe_experts), vp, vp, vp, sz, vp]
         for n in ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_bf16", "moe_combine", "moe_forward",
                   "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_forward_shard",
-                  "moe_add_rmsnorm", "moe_mlp"):
+                  "moe_forward_fused", "moe_forward_fused_status", "moe_add_rmsnorm", "moe_mlp"):
             getattr(L, n).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -227,6 +233,30 @@ def mlp_workspace(d_model: int, inter: int, tokens: int, device="cuda") -> torch
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
 
 
+def moe_forward_fused_workspace_size(dims: moe_dims, tokens: int) -> int:
+    return int(lib().moe_forward_fused_workspace_size(ctypes.byref(dims), int(tokens)))
+
+
+def fused_workspace(dims: moe_dims, tokens: int, device="cuda") -> torch.Tensor:
+    """Workspace of moe_forward_fused for up to `tokens` tokens, zeroed (its
+    leading control block must start at zero; each call leaves it so)."""
+    n = moe_forward_fused_workspace_size(dims, tokens)
+    if n == 0:
+        raise MoeError(-2, "moe_forward_fused_workspace_size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_forward_fused(dims, weights: moe_weights, tokens, x, delta, idx_out, w_out, ws, stream=None):
+    _check(lib().moe_forward_fused(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta),
+                                   _p(idx_out), _p(w_out), _p(ws), ws.numel() if ws is not None else 0,
+                                   _stream(stream)), "moe_forward_fused")
+
+
+def moe_forward_fused_status(ws, stream=None) -> int:
+    """MOE_OK, or MOE_ERR_STALLED if a wait of the last call on `ws` gave up (synchronises the stream)."""
+    return int(lib().moe_forward_fused_status(_p(ws), _stream(stream)))
+
+
 def moe_mlp(d_model, inter, tokens, mlp: moe_experts, x, out, ws, stream=None):
     _check(lib().moe_mlp(int(d_model), int(inter), int(tokens), ctypes.byref(mlp), _p(x), _p(out), _p(ws),
                          ws.numel() if ws is not None else 0, _stream(stream)), "moe_mlp")
@@ -275,6 +305,7 @@ class MoELayer:
                 experts_struct(*(params[k] for k in _EXPERT_KEYS)),
                 experts_struct(*(params["sh_" + k] for k in _EXPERT_KEYS)))
         self._ws: Optional[torch.Tensor] = None
+        self._fused_ws: Optional[torch.Tensor] = None
 
     def workspace(self, tokens: int) -> torch.Tensor:
         n = moe_workspace_size(self.dims, tokens)
@@ -290,6 +321,21 @@ class MoELayer:
             delta = torch.empty_like(x)
         run = moe_forward_bf16 if self.bf16 else moe_forward
         run(self.dims, self.weights, T, x, delta, idx, w, self.workspace(T), stream)
+        return delta
+
+    def forward_fused(self, x: torch.Tensor, delta=None, idx=None, w=None, stream=None) -> torch.Tensor:
+        """forward() as one kernel launch (moe_forward_fused): e4m3 weights, at most 64 tokens."""
+        if self.bf16:
+            raise ValueError("the single-launch forward takes e4m3 expert weights")
+        if x.dtype != torch.bfloat16 or x.dim() != 2 or x.shape[1] != self.dims.d_model or not x.is_contiguous():
+            raise ValueError("x must be a contiguous bf16 [tokens, d_model] tensor")
+        T = x.shape[0]
+        if delta is None:
+            delta = torch.empty_like(x)
+        n = moe_forward_fused_workspace_size(self.dims, T)
+        if self._fused_ws is None or self._fused_ws.numel() < n:
+            self._fused_ws = fused_workspace(self.dims, T, device=self.params["gate_w"].device)
+        moe_forward_fused(self.dims, self.weights, T, x, delta, idx, w, self._fused_ws, stream)
         return delta
 
     __call__ = forward

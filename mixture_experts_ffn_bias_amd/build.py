@@ -18,7 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "gate.hip", "permute.hip", "ffn.hip", "combine.hip", "norm.hip"]
+SOURCES = ["api.hip", "gate.hip", "permute.hip", "ffn.hip", "combine.hip", "norm.hip", "decode.hip"]
 ARCH = "gfx950"
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function",

@@ -11,6 +11,12 @@ using namespace moe;
 
 namespace {
 
+#define MOE_TRY(expr)            \
+  do {                           \
+    const int st_ = (expr);      \
+    if (st_ != MOE_OK) return st_; \
+  } while (0)
+
 constexpr size_t WS_ALIGN = 256;
 constexpr int MAX_FEATURES = 32768;  // keeps every row offset and grid size well inside int32
 
@@ -47,6 +53,41 @@ Layout layout(const moe_dims& dm, int64_t T) {
   L.xq = take(t * d);
   L.xs = take(t * (d / BLK) * 4);
   L.hq = take(rows * I * 2);  // e4m3 h, or bf16 h with bf16 expert weights
+  L.hs = take(rows * (I / BLK) * 4);
+  L.rows = take(rows * d * 2);
+  L.total = off;
+  return L;
+}
+
+// Single-launch forward: the control block first, then what the steps pass on.
+struct FusedLayout {
+  size_t ctl, zpart, idx, w, counts, offsets, row_token, pair_row, tiles, n_tiles, xq, xs, hq, hs, rows, total;
+};
+
+FusedLayout fused_layout(const moe_dims& dm, int64_t T) {
+  FusedLayout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  const size_t E = dm.n_experts, K = dm.topk, d = dm.d_model, I = dm.inter, t = (size_t)T;
+  const size_t rows = t * K + t;
+  const DecodeShape sh = decode_shape((int)T, dm.d_model, dm.inter, dm.n_experts, dm.topk);
+  L.ctl = take(DEC_CTL_INTS * 4);
+  L.zpart = take((size_t)2 * sh.gate_kz * t * E * 4);
+  L.idx = take(t * K * 4);
+  L.w = take(t * K * 4);
+  L.counts = take(E * 4);
+  L.offsets = take((E + 1) * 4);
+  L.row_token = take(rows * 4);
+  L.pair_row = take(t * K * 4);
+  L.tiles = take((size_t)sh.max_tiles * sizeof(int4));
+  L.n_tiles = take(4);
+  L.xq = take(t * d);
+  L.xs = take(t * (d / BLK) * 4);
+  L.hq = take(rows * I);
   L.hs = take(rows * (I / BLK) * 4);
   L.rows = take(rows * d * 2);
   L.total = off;
@@ -107,6 +148,17 @@ int check_tokens(const moe_dims& d, int64_t T) {
   return MOE_OK;
 }
 
+int check_fused(const moe_dims* dims, int64_t T) {
+  MOE_TRY(check_dims(dims));
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T > DEC_MAX_TOKENS) return MOE_ERR_UNSUPPORTED;
+  if (T > 0) {
+    const DecodeShape sh = decode_shape((int)T, dims->d_model, dims->inter, dims->n_experts, dims->topk);
+    if (DEC_CTL_UP + sh.max_tiles > DEC_CTL_INTS) return MOE_ERR_UNSUPPORTED;
+  }
+  return MOE_OK;
+}
+
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int check_experts(const moe_experts* x) {
@@ -134,12 +186,6 @@ T* at(void* ws, size_t off) {
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
-
-#define MOE_TRY(expr)            \
-  do {                           \
-    const int st_ = (expr);      \
-    if (st_ != MOE_OK) return st_; \
-  } while (0)
 
 }  // namespace
 
@@ -406,6 +452,60 @@ int moe_forward_shard(const moe_dims* dims, const moe_weights* weights, int64_t 
                                            expert_end, d.d_model, y_partial, s));
 }
 
+size_t moe_forward_fused_workspace_size(const moe_dims* dims, int64_t tokens) {
+  if (check_fused(dims, tokens) != MOE_OK || tokens == 0) return 0;
+  return fused_layout(*dims, tokens).total;
+}
+
+int moe_forward_fused(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
+                      uint16_t* delta, int32_t* idx_out, float* w_out, void* workspace, size_t workspace_bytes,
+                      void* stream) {
+  MOE_TRY(check_fused(dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  if (!weights || !weights->gate_w || !weights->gate_b || !x || !delta) return MOE_ERR_INVALID_ARG;
+  MOE_TRY(check_experts(&weights->routed));
+  MOE_TRY(check_experts(&weights->shared));
+  if (!aligned(x, 16) || !aligned(delta, 16) || !aligned(weights->gate_w, 16) || !aligned(weights->gate_b, 4) ||
+      (idx_out && !aligned(idx_out, 4)) || (w_out && !aligned(w_out, 4)))
+    return MOE_ERR_ALIGN;
+  const FusedLayout L = fused_layout(*dims, tokens);
+  if (!workspace || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+  if (!aligned(workspace, WS_ALIGN)) return MOE_ERR_ALIGN;
+  const moe_dims& d = *dims;
+  const int T = (int)tokens;
+  const DecodeShape sh = decode_shape(T, d.d_model, d.inter, d.n_experts, d.topk);
+  DecodeBufs b;
+  b.ctl = at<int>(workspace, L.ctl);
+  b.zpart = at<float>(workspace, L.zpart);
+  b.idx = idx_out ? idx_out : at<int32_t>(workspace, L.idx);
+  b.w = w_out ? w_out : at<float>(workspace, L.w);
+  b.counts = at<int32_t>(workspace, L.counts);
+  b.offsets = at<int32_t>(workspace, L.offsets);
+  b.row_token = at<int32_t>(workspace, L.row_token);
+  b.pair_row = at<int32_t>(workspace, L.pair_row);
+  b.tiles = at<int4>(workspace, L.tiles);
+  b.n_tiles = at<int32_t>(workspace, L.n_tiles);
+  b.xq = at<uint8_t>(workspace, L.xq);
+  b.xs = at<float>(workspace, L.xs);
+  b.hq = at<uint8_t>(workspace, L.hq);
+  b.hs = at<float>(workspace, L.hs);
+  b.rows = at<uint16_t>(workspace, L.rows);
+  return hip_status(launch_decode(sh, ptrs(weights->routed), ptrs(weights->shared), x, weights->gate_w,
+                                  weights->gate_b, T, d.d_model, d.inter, d.n_experts, d.n_groups, d.topk_groups,
+                                  d.topk, d.route_scale, b, delta, (hipStream_t)stream));
+}
+
+int moe_forward_fused_status(const void* workspace, void* stream) {
+  if (!workspace) return MOE_ERR_INVALID_ARG;
+  int32_t st = 0;
+  const hipStream_t s = (hipStream_t)stream;
+  if (hipMemcpyAsync(&st, static_cast<const int32_t*>(workspace) + DEC_CTL_STATUS, sizeof(st),
+                     hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return st == 0 ? MOE_OK : MOE_ERR_STALLED;
+}
+
 int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* residual, const float* gain, float eps,
                     uint16_t* out, void* stream) {
   if (d <= 0 || tokens < 0 || !(eps >= 0.f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
@@ -451,6 +551,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_ALIGN: return "misaligned pointer";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_STALLED: return "a wait in the single-launch forward gave up (outputs not valid)";
     default: return "unknown status";
   }
 }

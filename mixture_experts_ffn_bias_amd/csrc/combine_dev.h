@@ -1,0 +1,123 @@
+// Router-weighted combine and shared-expert add ("DeepSeek-V3.2-Exp · MoE
+// update", moe-forward excerpt: ``y[idx] += expert(x[idx]) * weights[idx, top]``
+// over experts in ascending id into an fp32 accumulator, ``y +=
+// shared_experts(x)``, then the cast back to the input dtype;
+// "DeepSeek-V3.2-Exp · Add shared output", formula).
+//
+// One workgroup per token and share of the row (small batches split each row
+// over several workgroups to occupy the chip); the token's K rows are visited
+// in ascending expert id, so the fp32 sum has the same order as the pages'
+// loop and the result is deterministic (no atomics).
+//
+// The partial form serves one rank of an expert-parallel layer: it sums only
+// the experts [e_lo, e_hi) a rank holds (the pages' experts_start_idx ..
+// experts_end_idx slice) and leaves y in fp32 for the cross-rank sum.
+//
+// Device function shared by the combine kernels and the single-launch layer
+// kernel.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+// PARTIAL: y (fp32) = the sum over choices with expert in [e_lo, e_hi), plus
+// the shared row when has_shared; otherwise delta (bf16) = bf16(full sum).
+// Token t, share `part` of `nparts` of the row (8-element chunks); called by
+// every thread of the workgroup (K <= 32 <= blockDim.x).  COH: the routing
+// and the rows are read with agent-coherent loads (common.h, ld / st).
+struct CombineLds {
+  int row[32];
+  float w[32];
+  int e[32];
+  int n;
+};
+
+template <bool PARTIAL, bool COH = false>
+__device__ __forceinline__ void combine_token(const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                              const int32_t* __restrict__ pair_row,
+                                              const uint16_t* __restrict__ rows, int has_shared, int T, int K,
+                                              int e_lo, int e_hi, int d, void* __restrict__ out, int t, int part,
+                                              int nparts, CombineLds& L) {
+  int* s_row = L.row;
+  float* s_w = L.w;
+  int* s_e = L.e;
+  int& s_n = L.n;
+  const int64_t TK = (int64_t)T * K;
+  // the token's choices in the range, loaded in parallel and placed by rank in
+  // ascending expert id (equal ids keep their order); others are left out
+  const int me = threadIdx.x;
+  int e = 0, row = 0;
+  float wk = 0.f;
+  bool in = false;
+  if (me < K) {
+    e = ld<COH>(idx + (size_t)t * K + me);
+    in = e >= e_lo && e < e_hi;
+    row = ld<COH>(pair_row + (size_t)t * K + me);
+    row = row < 0 ? 0 : (row >= TK ? (int)(TK - 1) : row);
+    wk = ld<COH>(w + (size_t)t * K + me);
+    s_e[me] = in ? e : 0x7fffffff;
+  }
+  __syncthreads();
+  if (me < K && in) {
+    int rank = 0;
+    for (int j = 0; j < K; ++j) {
+      const int o = s_e[j];
+      rank += (o < e || (o == e && j < me)) ? 1 : 0;
+    }
+    s_row[rank] = row;
+    s_w[rank] = wk;
+  }
+  if (me == 0) {
+    int n = 0;
+    for (int j = 0; j < K; ++j) n += s_e[j] != 0x7fffffff ? 1 : 0;
+    s_n = n;
+  }
+  __syncthreads();
+  const int n = s_n;
+  // this workgroup's share of the row: 8-element chunks [c0, c1)
+  const int nch = d / 8;
+  const int per = (nch + nparts - 1) / nparts;
+  const int c0 = part * per, c1 = min(nch, c0 + per);
+  for (int c = c0 + threadIdx.x; c < c1; c += blockDim.x) {
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = 0.f;
+    for (int k = 0; k < n; ++k) {
+      const uint4 v = ld16<COH>(rows + (size_t)s_row[k] * d + c * 8);
+      const float wk = s_w[k];
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[2 * i] = fmaf(wk, bf16_to_f32(u[i] & 0xFFFFu), y[2 * i]);
+        y[2 * i + 1] = fmaf(wk, bf16_to_f32(u[i] >> 16), y[2 * i + 1]);
+      }
+    }
+    if (has_shared) {
+      const uint4 v = ld16<COH>(rows + (size_t)(TK + t) * d + c * 8);
+      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y[2 * i] += bf16_to_f32(u[i] & 0xFFFFu);
+        y[2 * i + 1] += bf16_to_f32(u[i] >> 16);
+      }
+    }
+    if constexpr (PARTIAL) {
+      float4* dst = (float4*)((float*)out + (size_t)t * d + c * 8);
+      dst[0] = make_float4(y[0], y[1], y[2], y[3]);
+      dst[1] = make_float4(y[4], y[5], y[6], y[7]);
+    } else {
+      uint4 o;
+      o.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+      o.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+      o.z = (uint32_t)f32_to_bf16(y[4]) | ((uint32_t)f32_to_bf16(y[5]) << 16);
+      o.w = (uint32_t)f32_to_bf16(y[6]) | ((uint32_t)f32_to_bf16(y[7]) << 16);
+      *(uint4*)((uint16_t*)out + (size_t)t * d + c * 8) = o;
+    }
+  }
+}
+
+}  // namespace
+
+}  // namespace moe

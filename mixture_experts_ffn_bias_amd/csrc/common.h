@@ -82,6 +82,57 @@ __device__ __forceinline__ FragH as_bf16(v8i q) {
   return f;
 }
 
+// Accesses of data that another workgroup of the same launch produces or
+// consumes (the single-launch layer kernel).  COH = true: agent-coherent
+// loads and stores (relaxed agent-scope atomics: global_load / global_store
+// with sc1), which read and write at the point where all XCDs see the same
+// memory, so no L2 writeback or invalidation is needed around the completion
+// counts that order them.  COH = false: plain accesses.
+template <bool COH, typename T>
+__device__ __forceinline__ T ld(const T* p) {
+  if constexpr (COH)
+    return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    return *p;
+}
+
+template <bool COH, typename T>
+__device__ __forceinline__ void st(T* p, T v) {
+  if constexpr (COH)
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else
+    *p = v;
+}
+
+// 8 and 16 bytes (16-byte aligned for ld16 / st16); COH: as 8-byte halves.
+template <bool COH>
+__device__ __forceinline__ void st8(void* p, uint2 v) {
+  if constexpr (COH)
+    st<true>((uint64_t*)p, __builtin_bit_cast(uint64_t, v));
+  else
+    *(uint2*)p = v;
+}
+
+template <bool COH>
+__device__ __forceinline__ uint4 ld16(const void* p) {
+  if constexpr (COH) {
+    const uint64_t lo = ld<true>((const uint64_t*)p), hi = ld<true>((const uint64_t*)p + 1);
+    return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
+  } else {
+    return *(const uint4*)p;
+  }
+}
+
+template <bool COH>
+__device__ __forceinline__ void st16(void* p, uint4 v) {
+  if constexpr (COH) {
+    st<true>((uint64_t*)p, (uint64_t)v.x | ((uint64_t)v.y << 32));
+    st<true>((uint64_t*)p + 1, (uint64_t)v.z | ((uint64_t)v.w << 32));
+  } else {
+    *(uint4*)p = v;
+  }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   return v;

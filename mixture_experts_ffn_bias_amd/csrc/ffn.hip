@@ -14,20 +14,12 @@
 // acc += P * (s_weight[block] * s_act[row, block]).
 // Weights are the A operand (16 output features), activations the B operand
 // (16 rows); lane l ends with features 4*(l/16)+j of row l%16.
-#include "common.h"
-#include "kernels.h"
+#include "ffn_tile.h"
 #include "plan.h"
 
 namespace moe {
 
 namespace {
-
-__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
-
-// token of permuted row `row` (NULL map: rows are tokens, as for a dense MLP)
-__device__ __forceinline__ int token_of(const int32_t* row_token, int row, int T) {
-  return row_token ? clampi(row_token[row], 0, T - 1) : row;
-}
 
 // One block of 256 threads: the tile list from the expert offsets
 // (plan_tiles_block).  The shared expert's tiles come first: they hold the
@@ -47,568 +39,16 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
   plan_tiles_block(lo, cnt, T, K, NT, has_shared, cap, e_lo, e_hi, s, tiles, n_tiles);
 }
 
-// With e4m3 weights, xq/hq are e4m3 rows with block scales xs/hs; with bf16
-// weights (no scales), xq is the bf16 input x, hq receives bf16 h and the
-// scale pointers are unused.
-struct FfnArgs {
-  ExpertPtrs routed;
-  ExpertPtrs shared;
-  int E, d, I, T, K;
-  const int4* tiles;
-  const int32_t* n_tiles;
-  const int32_t* row_token;
-  const uint8_t* xq;
-  const float* xs;
-  uint8_t* hq;
-  float* hs;
-  uint16_t* out;
-};
-
-// ---------------------------------------------------------------------------
-// LDS-tiled kernels.  A workgroup (8 waves) owns one tile of up to 128 rows
-// and 256 weight rows in two groups of 128:
-//   up-projection:   group 0 = w1 rows of one 128-wide h block, group 1 = the
-//                    w3 rows of the same block (so g and u of an h column meet
-//                    in the same lane and the epilogue fuses SwiGLU + h quant);
-//   down-projection: two consecutive 128-feature blocks of w2.
-// Per 128-deep K block, the e4m3 weight (256 x 128 B) and activation
-// (128 x 128 B) tiles and the activation scales are copied global -> LDS
-// directly (global_load_lds, no register staging) into one of three stage
-// buffers, two K blocks ahead of the multiply.  Rows are stored unpadded with
-// their 16-byte chunks XOR-permuted (swz), which makes the MFMA-layout reads
-// bank-conflict free.  Wave (wr, wc) multiplies rows [64 wr, 64 wr + 64) by
-// weight rows {32 wc .. 32 wc + 31} of both groups: 4 x 4 block products per
-// K block.
-// The weight copies of a tile that is the only one of its expert (every tile
-// when T <= 128) carry the non-temporal hint: those bytes are read exactly
-// once, and full-line DMA streams with the hint reach a markedly higher HBM
-// read rate on gfx950 (about 7.0 against 6.2 TB/s in a plain read test).
-// Weights that other tiles read again are loaded with the default policy so
-// that the L2 can serve the repeat reads.
-// ---------------------------------------------------------------------------
-
-constexpr int TT_WROWS = 256;                // weight rows per tile
-constexpr int TT_A_BYTES = TT_WROWS * BLK;   // one K block of the weight tile
-constexpr int CPOL_NT = 2;                   // cache-policy bits of a non-temporal load (gfx94x/gfx950)
-
-// Shape of the LDS pipeline for tiles of ROWS activation rows.  A stage holds
-// one K block: the 256 weight rows, the ROWS activation rows and their scales.
-//   ROWS = 128: three stages (two K blocks in flight), one workgroup per CU.
-//   ROWS = 32 (small batches, where the weights are the traffic): two stages
-//     of 36 KiB and at most 128 VGPRs, so two workgroups share a CU and one's
-//     start-up and epilogue overlap the other's weight stream.
-template <int ROWS>
-struct Tile {
-  static_assert(ROWS == 32 || ROWS == 128, "tile rows");
-  static constexpr int B_BYTES = ROWS * BLK;
-  static constexpr int S_BYTES = ROWS * 4;
-  static constexpr int STAGE = TT_A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int NSTAGE = ROWS == 128 ? 3 : 2;
-  static constexpr int SMEM = NSTAGE * STAGE;
-  static constexpr int OCC = ROWS == 128 ? 1 : 2;       // workgroups per CU (8 waves each: 2 OCC waves per SIMD)
-  static constexpr int APW = ROWS == 128 ? 2 : 1;       // 8-row activation pieces per copying wave
-  static constexpr int AWAVES = ROWS / (8 * APW);       // waves that copy activation rows
-  static constexpr int SWAVES = (ROWS + 63) / 64;       // waves that copy activation scales (64 rows each)
-  static constexpr int MVMAX = ROWS >= 64 ? 4 : ROWS / 16;  // 16-row sub-tiles per wave
-};
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef __attribute__((address_space(1))) void* gbl_ptr_t;
-// Read-only data addressed uniformly by the workgroup (the weight block
-// scales): loads through the constant address space become scalar loads,
-// which are counted apart from the vector-memory copies the pipeline waits on.
-typedef const __attribute__((address_space(4))) float* const_f32_ptr;
-
-// LDS holds each 128-byte row unpadded with its 16-byte chunks permuted:
-// chunk c of row r sits at slot c ^ swz(r).  Sixteen consecutive rows then
-// spread one MFMA-layout read (same chunk, rows r0..r0+15) over all banks.
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
-
-// Wait until at most N of this wave's vector-memory operations are pending.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
-}
-
-// Global -> LDS copies (global_load_lds) of one K block.  Wave w copies
-// weight rows [32w, 32w + 32) (four 8-row pieces), the APW 8-row activation
-// pieces [APW w, APW w + APW) (waves w < AWAVES) and, e4m3 only, for
-// w < SWAVES the scales of activation rows [64w, 64w + 64).  Lane l of a
-// piece covers row piece_row0 + l/8 and LDS slot l%8, so it fetches global
-// chunk (l%8) ^ swz(row).
-template <int ROWS>
-struct TileSrc {
-  const uint8_t* a[4];                // this lane's source rows for the four weight pieces (chunk applied)
-  const uint8_t* b[Tile<ROWS>::APW];  // ... for this wave's activation pieces
-  const float* s;                     // scale row of activation row 64w + lane (waves w < SWAVES)
-};
-
-// act (wave-uniform): this wave's activation pieces hold rows some MFMA
-// reads; otherwise they are not copied.
-template <int ROWS, bool BF>
-__device__ __forceinline__ int tile_copies(int wave, bool act) {
-  using G = Tile<ROWS>;
-  return 4 + (act ? G::APW : 0) + (!BF && wave < G::SWAVES ? 1 : 0);
-}
-
-template <int ROWS, bool BF, int WPOL>
-__device__ __forceinline__ void tile_issue(const TileSrc<ROWS>& src, uint8_t* stage, int kb, int wave, bool act) {
-  using G = Tile<ROWS>;
-  const int off = kb * BLK;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.a[i] + off), (lds_ptr_t)(stage + (wave * 4 + i) * 1024), 16, 0,
-                                     WPOL);
-  if (act) {
-#pragma unroll
-    for (int j = 0; j < G::APW; ++j)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[j] + off),
-                                       (lds_ptr_t)(stage + TT_A_BYTES + (wave * G::APW + j) * 1024), 16, 0, 0);
-  }
-  if (!BF && wave < G::SWAVES) {
-    if (ROWS >= 64 || (threadIdx.x & 63) < ROWS)
-      __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.s + kb),
-                                       (lds_ptr_t)(stage + TT_A_BYTES + G::B_BYTES + wave * 256), 4, 0, 0);
-  }
-}
-
-// Wait until at most n of this wave's vector-memory operations are pending
-// (n wave-uniform, 0 <= n <= 14; larger values wait for all).
-__device__ __forceinline__ void wait_vmcnt_upto(int n) {
-  switch (__builtin_amdgcn_readfirstlane(n)) {
-    case 4: wait_vmcnt<4>(); break;
-    case 5: wait_vmcnt<5>(); break;
-    case 6: wait_vmcnt<6>(); break;
-    case 7: wait_vmcnt<7>(); break;
-    case 8: wait_vmcnt<8>(); break;
-    case 10: wait_vmcnt<10>(); break;
-    case 12: wait_vmcnt<12>(); break;
-    case 14: wait_vmcnt<14>(); break;
-    default: wait_vmcnt<0>(); break;
-  }
-}
-
-// Workgroup barrier of the copy pipeline.  Each wave has already waited
-// (wait_vmcnt) for its own global->LDS copies of the stage the barrier
-// publishes, and the pipeline writes LDS in no other way, so no memory fence
-// is needed: the fence __syncthreads adds would also wait for the copies of
-// the stage after it.  The empty asm statements keep the compiler from moving
-// LDS accesses across the barrier.
-__device__ __forceinline__ void pipeline_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-__device__ __forceinline__ v8i lds_frag(const uint8_t* base, int r, int g) {
-  const uint8_t* row = base + r * BLK;
-  const int z = swz(r);
-  const v4i lo = *(const v4i*)(row + 16 * (g ^ z));
-  const v4i hi = *(const v4i*)(row + 16 * ((4 + g) ^ z));
-  return v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-}
-
-// One K block of the tile: this wave's block products from the stage buffer
-// `stage`, scaled and added to acc (MV: the wave's 16-row sub-tiles that hold
-// rows; 0 multiplies nothing).
-template <int ROWS, bool BF, int MV>
-__device__ __forceinline__ void kblock_multiply(const uint8_t* stage, const_f32_ptr sa0, const_f32_ptr sa1, int kb,
-                                                v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
-  using G = Tile<ROWS>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int wr = wave >> 2, wc = wave & 3;
-  if constexpr (BF && MV > 0) {
-    // bf16 operands: the 128 bytes of a row are 64 k values, two MFMAs per block, no scales
-    const uint8_t* la = stage;
-    const uint8_t* lb = la + TT_A_BYTES;
-    FragH B[MV];
-#pragma unroll
-    for (int m = 0; m < MV; ++m) B[m] = as_bf16(lds_frag(lb, wr * 64 + 16 * m + r, g));
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const FragH A = as_bf16(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-          for (int m = 0; m < MV; ++m)
-            acc[gi][jt][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], acc[gi][jt][m], 0, 0, 0);
-      }
-    }
-  }
-  if constexpr (!BF && MV > 0) {
-    const uint8_t* la = stage;
-    const uint8_t* lb = la + TT_A_BYTES;
-    const float* ls = (const float*)(lb + G::B_BYTES);
-    const float s_a0 = sa0[kb], s_a1 = sa1[kb];
-    Frag B[MV];
-    float sb[MV];
-#pragma unroll
-    for (int m = 0; m < MV; ++m) {
-      B[m] = decode_e4m3(lds_frag(lb, wr * 64 + 16 * m + r, g));
-      sb[m] = ls[wr * 64 + 16 * m + r];
-    }
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        const Frag A = decode_e4m3(lds_frag(la, gi * 128 + wc * 32 + jt * 16 + r, g));
-        const float sg = gi == 0 ? s_a0 : s_a1;
-        // MV independent accumulation chains, issued round-robin
-        v4f p[MV];
-#pragma unroll
-        for (int m = 0; m < MV; ++m) p[m] = v4f{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int m = 0; m < MV; ++m) p[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.k[q], B[m].k[q], p[m], 0, 0, 0);
-#pragma unroll
-        for (int m = 0; m < MV; ++m) {
-          const float f = sg * sb[m];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[gi][jt][m][j] = fmaf(p[m][j], f, acc[gi][jt][m][j]);
-        }
-      }
-    }
-  }
-}
-
-// Main loop shared by both projections.  src: this lane's DMA sources.
-// sa0, sa1: weight block scales of the two weight groups over K.
-// acc[gi][jt][m].  MV: the 16-row sub-tiles of this wave that hold rows
-// (0..4; a compile-time count keeps the K-block body free of branches, so the
-// LDS reads, decodes and MFMAs of a block can be interleaved).  WPOL: cache
-// policy of the weight copies.
-template <int ROWS, bool BF, int MV, int WPOL>
-__device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS>& src, const_f32_ptr sa0,
-                                               const_f32_ptr sa1, int nkb, int nrows,
-                                               v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
-  using G = Tile<ROWS>;
-  constexpr int AHEAD = G::NSTAGE - 1;  // K blocks whose copies are in flight during a multiply
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int wr = wave >> 2, wc = wave & 3;
-
-  const bool act = wave < G::AWAVES && 16 * ((wave * G::APW * 8) >> 4) < nrows;
-  const int per_stage = tile_copies<ROWS, BF>(wave, act);
-  int issued = 0;
-#pragma unroll
-  for (int k = 0; k < AHEAD; ++k) {
-    if (k < nkb) {
-      tile_issue<ROWS, BF, WPOL>(src, smem + k * G::STAGE, k, wave, act);
-      ++issued;
-    }
-  }
-  wait_vmcnt_upto(per_stage * (issued - 1));
-  pipeline_barrier();
-
-  // Iteration kb issues the copies of block kb + AHEAD into the stage that
-  // block kb - 1 used (every wave left it at the last barrier), multiplies
-  // block kb, then waits for its own copies of block kb + 1 (all but those of
-  // the blocks issued after it); the barrier publishes that stage.
-  int cur = 0;  // stage buffer holding K block kb
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + AHEAD < nkb) {
-      const int nb = cur == 0 ? G::NSTAGE - 1 : cur - 1;  // (kb + AHEAD) % NSTAGE
-      tile_issue<ROWS, BF, WPOL>(src, smem + nb * G::STAGE, kb + AHEAD, wave, act);
-    }
-    // a wave whose 64 rows hold no tile row (MV = 0) only helps with the copies
-    kblock_multiply<ROWS, BF, MV>(smem + cur * G::STAGE, sa0, sa1, kb, acc);
-    if (kb + 1 < nkb) wait_vmcnt_upto(per_stage * (min(kb + AHEAD, nkb - 1) - kb - 1));
-    pipeline_barrier();
-    cur = cur == G::NSTAGE - 1 ? 0 : cur + 1;
-  }
-}
-
-template <int ROWS, bool BF, int WPOL>
-__device__ __forceinline__ void run_mainloop_pol(uint8_t* smem, const TileSrc<ROWS>& src, const_f32_ptr c0,
-                                                 const_f32_ptr c1, int nkb, int nrows, int mvalid,
-                                                 v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
-  if constexpr (Tile<ROWS>::MVMAX == 4) {
-    switch (mvalid) {
-      case 0: tiled_mainloop<ROWS, BF, 0, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      case 1: tiled_mainloop<ROWS, BF, 1, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      case 2: tiled_mainloop<ROWS, BF, 2, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      case 3: tiled_mainloop<ROWS, BF, 3, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      default: tiled_mainloop<ROWS, BF, 4, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    }
-  } else {
-    switch (mvalid) {
-      case 0: tiled_mainloop<ROWS, BF, 0, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      case 1: tiled_mainloop<ROWS, BF, 1, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      default: tiled_mainloop<ROWS, BF, 2, WPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-    }
-  }
-}
-
-// The main loop for this tile (mvalid: wave-uniform count of this wave's
-// 16-row sub-tiles that hold rows), with non-temporal weight copies when the
-// tile reads them once.
-template <int ROWS, bool BF>
-__device__ __forceinline__ void run_mainloop(uint8_t* smem, const TileSrc<ROWS>& src, const float* sa0,
-                                             const float* sa1, int nkb, int nrows, int mvalid, bool once,
-                                             v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
-  const const_f32_ptr c0 = (const_f32_ptr)sa0, c1 = (const_f32_ptr)sa1;
-  if (once)
-    run_mainloop_pol<ROWS, BF, CPOL_NT>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
-  else
-    run_mainloop_pol<ROWS, BF, 0>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
-}
-
-// DMA source pointers of this lane.  wrow(i): weight row of tile row i
-// (0..255); arow(j): activation row pointer of tile row j (0..127);
-// srow(j): its scale row.
-template <int ROWS, typename WRow, typename ARow, typename SRow>
-__device__ __forceinline__ TileSrc<ROWS> make_tile_src(WRow wrow, ARow arow, SRow srow) {
-  using G = Tile<ROWS>;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int slot = lane & 7;
-  TileSrc<ROWS> t;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = (wave * 4 + i) * 8 + (lane >> 3);
-    t.a[i] = wrow(row) + 16 * (slot ^ swz(row));
-  }
-#pragma unroll
-  for (int j = 0; j < G::APW; ++j) {
-    const int row = min((wave * G::APW + j) * 8 + (lane >> 3), ROWS - 1);
-    t.b[j] = arow(row) + 16 * (slot ^ swz(row));
-  }
-  t.s = srow(min(min(wave, G::SWAVES - 1) * 64 + lane, ROWS - 1));
-  return t;
-}
-
-// LDS exchange barrier: this wave's LDS stores are complete (lgkmcnt) and
-// every wave has arrived.  Unlike __syncthreads it does not wait for the
-// wave's global -> LDS copies, which may still be in flight for the next
-// K block.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// One work item of a projection: a tile and a block of output columns.
-template <int ROWS>
-struct Item {
-  TileSrc<ROWS> src;   // this lane's copy sources
-  const float* sa0;    // weight block scales of the two weight groups over K (e4m3)
-  const float* sa1;
-  int blk;             // up: the 128-wide h block; down: the pair of 128-feature output blocks
-  int row0, nrows;     // the tile's permuted rows
-  bool once;           // the tile is the only one of its expert
-};
-
-// Item `item` of the up-projection (tile item / nib, h block item % nib);
-// false past the last tile.
-template <int ROWS, bool BF>
-__device__ __forceinline__ bool up_item(const FfnArgs& a, int item, Item<ROWS>& it) {
-  constexpr int EB = BF ? 2 : 1;
-  const int nib = a.I / BLK, nkb = a.d * EB / BLK;
-  const int tile = item / nib, ib = item - tile * nib;
-  if (tile >= *a.n_tiles) return false;
-  const int4 td = a.tiles[tile];
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const bool sh = e >= a.E;
-  const ExpertPtrs& P = sh ? a.shared : a.routed;
-  const size_t eo = sh ? 0 : (size_t)e;
-  const int* rt = a.row_token;
-  it.src = make_tile_src<ROWS>(
-      [&](int row) {  // 0..127: w1 rows of block ib, 128..255: w3 rows
-        const uint8_t* base = row < 128 ? P.w1 : P.w3;
-        return base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d * EB;
-      },
-      [&](int row) {
-        const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T);
-        return a.xq + (size_t)tok * a.d * EB;
-      },
-      [&](int row) -> const float* {
-        if (BF) return nullptr;
-        const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T);
-        return a.xs + (size_t)tok * nkb;
-      });
-  it.sa0 = BF ? nullptr : P.s1 + (eo * nib + ib) * nkb;
-  it.sa1 = BF ? nullptr : P.s3 + (eo * nib + ib) * nkb;
-  it.blk = ib;
-  it.row0 = row0;
-  it.nrows = nrows;
-  it.once = td.w != 0;
-  return true;
-}
-
-// Item `item` of the down-projection (tile item / nob2, output blocks
-// 2 (item % nob2) and 2 (item % nob2) + 1); false past the last tile.
-template <int ROWS, bool BF>
-__device__ __forceinline__ bool down_item(const FfnArgs& a, int item, Item<ROWS>& it) {
-  constexpr int EB = BF ? 2 : 1;
-  const int nob = a.d / BLK, nkb = a.I * EB / BLK;
-  const int nob2 = (nob + 1) >> 1;
-  const int tile = item / nob2, ob = item - tile * nob2;
-  if (tile >= *a.n_tiles) return false;
-  const int4 td = a.tiles[tile];
-  const int e = td.x, row0 = td.y, nrows = td.z;
-  const bool sh = e >= a.E;
-  const ExpertPtrs& P = sh ? a.shared : a.routed;
-  const size_t eo = sh ? 0 : (size_t)e;
-  it.src = make_tile_src<ROWS>(
-      [&](int row) {  // a ragged last pair of blocks reads a valid row
-        const int o = min(ob * 256 + row, a.d - 1);
-        return P.w2 + (eo * a.d + o) * (size_t)a.I * EB;
-      },
-      [&](int row) { return a.hq + (size_t)(row0 + min(row, nrows - 1)) * a.I * EB; },
-      [&](int row) -> const float* {
-        return BF ? nullptr : a.hs + (size_t)(row0 + min(row, nrows - 1)) * nkb;
-      });
-  it.sa0 = BF ? nullptr : P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb;
-  it.sa1 = BF ? nullptr : P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb;
-  it.blk = ob;
-  it.row0 = row0;
-  it.nrows = nrows;
-  it.once = td.w != 0;
-  return true;
-}
-
-// 16-row sub-tiles of this wave that hold rows of the item (wave-uniform)
-template <int ROWS>
-__device__ __forceinline__ int item_mvalid(const Item<ROWS>& it) {
-  const int wr = (threadIdx.x >> 6) >> 2;
-  return __builtin_amdgcn_readfirstlane(min(Tile<ROWS>::MVMAX, max(0, (it.nrows - wr * 64 + 15) >> 4)));
-}
-
-// Up-projection epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32
-// columns of h block it.blk x its 64 rows; e4m3: per-row amax over the
-// block's 128 columns (4 waves) through `red` (2 KiB of LDS), then e4m3 h
-// and its scale; bf16: h itself.
-template <int ROWS, bool BF>
-__device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& it,
-                                            const v4f (&acc)[2][2][Tile<ROWS>::MVMAX], float* red) {
-  constexpr int MVX = Tile<ROWS>::MVMAX;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int wr = wave >> 2, wc = wave & 3;
-  const int nib = a.I / BLK;
-  if constexpr (BF) {
-#pragma unroll
-    for (int m = 0; m < MVX; ++m) {
-      const int rr = wr * 64 + 16 * m + r;
-      if (rr < it.nrows) {
-        const size_t row = (size_t)(it.row0 + rr);
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt) {
-          uint16_t hb[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float gv = round_bf16(acc[0][jt][m][j]);
-            const float uv = round_bf16(acc[1][jt][m][j]);
-            hb[j] = f32_to_bf16(gv / (1.f + expf(-gv)) * uv);
-          }
-          uint2 o;
-          o.x = (uint32_t)hb[0] | ((uint32_t)hb[1] << 16);
-          o.y = (uint32_t)hb[2] | ((uint32_t)hb[3] << 16);
-          *(uint2*)((uint16_t*)a.hq + row * a.I + it.blk * BLK + wc * 32 + jt * 16 + 4 * g) = o;
-        }
-      }
-    }
-    return;
-  }
-  float hv[2][MVX][4];
-#pragma unroll
-  for (int m = 0; m < MVX; ++m) {
-    float amax = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float gv = round_bf16(acc[0][jt][m][j]);
-        const float uv = round_bf16(acc[1][jt][m][j]);
-        const float h = round_bf16(gv / (1.f + expf(-gv)) * uv);
-        hv[jt][m][j] = h;
-        amax = fmaxf(amax, fabsf(h));
-      }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    if (g == 0) red[(wr * 4 + wc) * 64 + 16 * m + r] = amax;
-  }
-  lds_barrier();
-#pragma unroll
-  for (int m = 0; m < MVX; ++m) {
-    const int rr = wr * 64 + 16 * m + r;
-    if (rr < it.nrows) {
-      float amax = 0.f;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) amax = fmaxf(amax, red[(wr * 4 + c) * 64 + 16 * m + r]);
-      const float sc = amax == 0.f ? 1.f : amax / E4M3_MAX;
-      const size_t row = (size_t)(it.row0 + rr);
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-        *(uint32_t*)(a.hq + row * a.I + it.blk * BLK + wc * 32 + jt * 16 + 4 * g) =
-            pack4_e4m3(hv[jt][m][0] / sc, hv[jt][m][1] / sc, hv[jt][m][2] / sc, hv[jt][m][3] / sc);
-      if (wc == 0 && g == 0) a.hs[row * nib + it.blk] = sc;
-    }
-  }
-}
-
-// Down-projection epilogue: the wave's rows of output blocks 2 it.blk and
-// 2 it.blk + 1 (the second may lie past d), bf16.
-template <int ROWS>
-__device__ __forceinline__ void down_epilogue(const FfnArgs& a, const Item<ROWS>& it,
-                                              const v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
-  constexpr int MVX = Tile<ROWS>::MVMAX;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
-  const int wr = wave >> 2, wc = wave & 3;
-  const int nob = a.d / BLK;
-#pragma unroll
-  for (int m = 0; m < MVX; ++m) {
-    const int rr = wr * 64 + 16 * m + r;
-    if (rr < it.nrows) {
-      const size_t row = (size_t)(it.row0 + rr);
-#pragma unroll
-      for (int gi = 0; gi < 2; ++gi) {
-        if (2 * it.blk + gi < nob) {
-#pragma unroll
-          for (int jt = 0; jt < 2; ++jt) {
-            const v4f v = acc[gi][jt][m];
-            uint2 o;
-            o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-            o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-            *(uint2*)(a.out + row * a.d + (2 * it.blk + gi) * BLK + wc * 32 + jt * 16 + 4 * g) = o;
-          }
-        }
-      }
-    }
-  }
-}
-
-template <int ROWS>
-__device__ __forceinline__ void zero_acc(v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
-#pragma unroll
-  for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int m = 0; m < Tile<ROWS>::MVMAX; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
-}
-
 // One item per workgroup.  UP: grid = max_tiles * (I/128); down: grid =
 // max_tiles * ceil(d/256).  Block = 512.  BF: bf16 weights and activations
 // (64-element K blocks, no scales, h stored as bf16).
 template <bool UP, int ROWS, bool BF>
 __global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_tiled_kernel(FfnArgs a) {
-  using G = Tile<ROWS>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[G::SMEM];
-  constexpr int EB = BF ? 2 : 1;
-  const int nkb = (UP ? a.d : a.I) * EB / BLK;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<ROWS>::SMEM];
   Item<ROWS> it;
   if (!(UP ? up_item<ROWS, BF>(a, blockIdx.x, it) : down_item<ROWS, BF>(a, blockIdx.x, it)))
     return;  // uniform for the whole block, before any barrier
-  v4f acc[2][2][G::MVMAX];
-  zero_acc<ROWS>(acc);
-  run_mainloop<ROWS, BF>(smem, it.src, it.sa0, it.sa1, nkb, it.nrows, item_mvalid(it), it.once, acc);
-  if constexpr (UP)
-    up_epilogue<ROWS, BF>(a, it, acc, (float*)smem);  // the stage buffers are no longer read
-  else
-    down_epilogue<ROWS>(a, it, acc);
+  ffn_run_item<UP, ROWS, BF>(a, it, smem);
 }
 
 template <int ROWS, bool BF>

@@ -1,0 +1,242 @@
+// Router device functions ("DeepSeek-V3.2-Exp · MoE update", moe-forward
+// excerpt: the gate call; the router bias is implied by the MoE parameter
+// count on "MoE transformer block", parameter accounting table): partial
+// logits x . Wg^T on the matrix cores, sigmoid scores, bias for selection,
+// group-limited top-k and the normalised, scaled weights.  Shared by the
+// router kernels and the single-launch layer kernel.
+//
+// Logits: x is bf16, Wg is fp32.  Each fp32 weight is split into three bf16
+// parts hi + mid + lo that sum to it exactly, so three bf16 MFMAs per K step
+// give the fp32-weight product with fp32 accumulation.
+#pragma once
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+__device__ __forceinline__ void split3(float w, __bf16& hi, __bf16& mid, __bf16& lo) {
+  const uint32_t u = __float_as_uint(w);
+  const float h = __uint_as_float(u & 0xFFFF0000u);     // top 8 significant bits
+  const float r1 = w - h;                                // exact
+  const uint32_t u1 = __float_as_uint(r1);
+  const float m = __uint_as_float(u1 & 0xFFFF0000u);
+  const float r2 = r1 - m;                               // exact, fits in bf16
+  hi = __builtin_bit_cast(__bf16, (uint16_t)(u >> 16));
+  mid = __builtin_bit_cast(__bf16, (uint16_t)(u1 >> 16));
+  lo = (__bf16)r2;
+}
+
+// One wave: partial logits of tokens [t0, t0 + 16) (t0 < T; rows past T
+// repeat row T - 1 and are not stored) and nt (1..4) 16-expert tiles from e0,
+// over K range [k0, k1) (multiples of 32).  zp[t][e] (E columns) receives
+// the partial sums of this K range (COH: agent-coherent stores).
+template <bool COH = false>
+__device__ __forceinline__ void gate_logits_wave(const uint16_t* __restrict__ x, const float* __restrict__ gw,
+                                                 float* __restrict__ zp, int T, int d, int E, int t0, int e0,
+                                                 int nt, int k0, int k1) {
+  const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
+  const uint16_t* xr = x + (size_t)min(t0 + r, T - 1) * d;
+  const float* wr[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) wr[n] = gw + (size_t)(e0 + 16 * min(n, nt - 1) + r) * d;
+
+  v4f acc[4];
+#pragma unroll
+  for (int n = 0; n < 4; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
+
+  for (int k = k0; k < k1; k += 32) {
+    const v8bf a = *(const v8bf*)(xr + k + 8 * g);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      if (n < nt) {
+        const float4 f0 = *(const float4*)(wr[n] + k + 8 * g);
+        const float4 f1 = *(const float4*)(wr[n] + k + 8 * g + 4);
+        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+        v8bf hi, mid, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          __bf16 h, m, l;
+          split3(f[j], h, m, l);
+          hi[j] = h;
+          mid[j] = m;
+          lo[j] = l;
+        }
+        acc[n] = mfma_bf16(a, lo, acc[n]);
+        acc[n] = mfma_bf16(a, mid, acc[n]);
+        acc[n] = mfma_bf16(a, hi, acc[n]);
+      }
+    }
+  }
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    if (n < nt) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t0 + 4 * g + j;
+        if (t < T) st<COH>(zp + (size_t)t * E + e0 + 16 * n + r, acc[n][j]);
+      }
+    }
+  }
+}
+
+// LDS of one token's selection (E <= 256, G <= 64, K <= 32).
+struct GateSlot {
+  float score[256];   // sigmoid scores
+  float biased[256];  // scores + bias (NaN -> -inf), the selection key
+  float gs[64];       // group scores
+  int keep[64];       // group kept
+  float sel[32];      // scores of the chosen experts
+};
+
+// This wave's LDS writes are visible to all its lanes (the wave runs its LDS
+// operations in order; the fences keep the compiler from moving accesses).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Score of expert e from its logit z into the slot.
+__device__ __forceinline__ void gate_score(GateSlot& sl, const float* __restrict__ bias, int e, float z) {
+  const float s = 1.f / (1.f + expf(-z));
+  float v = s + bias[e];
+  if (v != v) v = -INFINITY;  // NaN never wins a comparison below
+  sl.score[e] = s;
+  sl.biased[e] = v;
+}
+
+// One wave: the logits of token tt from ksplit partial planes (plane stride
+// T*E), added in split order with eight splits of the lane's four experts
+// (lane, lane + 64, lane + 128, lane + 192) loaded before they are added,
+// then the scores into the slot (COH: agent-coherent loads).
+template <bool COH = false>
+__device__ __forceinline__ void gate_scores_wave(const float* __restrict__ zpart, int ksplit,
+                                                 const float* __restrict__ bias, int T, int E, int tt,
+                                                 GateSlot& sl) {
+  const int lane = threadIdx.x & 63;
+  const size_t split_stride = (size_t)T * E;
+  float z[4] = {0.f, 0.f, 0.f, 0.f};
+  const float* zp = zpart + (size_t)tt * E + lane;
+  int ks = 0;
+  for (; ks + 8 <= ksplit; ks += 8) {
+    float v[8][4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[j][i] = (lane + 64 * i < E) ? ld<COH>(zp + (ks + j) * split_stride + 64 * i) : 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] += v[j][i];
+  }
+  for (; ks < ksplit; ++ks)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (lane + 64 * i < E) z[i] += ld<COH>(zp + ks * split_stride + 64 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    if (e < E) gate_score(sl, bias, e, z[i]);
+  }
+}
+
+__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
+  return v > bv || (v == bv && i < bi);
+}
+
+// One wave, scores of token t in the slot: group score = sum of the two
+// largest biased scores of the group; the TG best groups are kept (ties to
+// the lower group); then K times the best remaining biased score among kept
+// experts (ties to the lower expert).  Weights = chosen sigmoid scores
+// normalised to sum 1, times route_scale.  live: store idx and w of token t
+// (COH: with agent-coherent stores).
+template <bool COH = false>
+__device__ __forceinline__ void gate_choose_wave(GateSlot& sl, int E, int G, int TG, int K, float route_scale,
+                                                 int t, bool live, int32_t* __restrict__ idx_out,
+                                                 float* __restrict__ w_out) {
+  const int lane = threadIdx.x & 63;
+  const int epg = E / G;
+  wave_lds_sync();
+  float b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    b[i] = e < E ? sl.biased[e] : -INFINITY;
+  }
+  if (lane < G) {
+    float m1 = -INFINITY, m2 = -INFINITY;
+    for (int j = 0; j < epg; ++j) {
+      const float v = sl.biased[lane * epg + j];
+      if (v > m1) {
+        m2 = m1;
+        m1 = v;
+      } else if (v > m2) {
+        m2 = v;
+      }
+    }
+    float gs = m1 + m2;
+    if (gs != gs) gs = -INFINITY;
+    sl.gs[lane] = gs;
+  }
+  wave_lds_sync();
+  if (lane < G) {
+    const float gs = sl.gs[lane];
+    int rank = 0;
+    for (int h = 0; h < G; ++h) {
+      const float o = sl.gs[h];
+      rank += (o > gs || (o == gs && h < lane)) ? 1 : 0;
+    }
+    sl.keep[lane] = rank < TG;
+  }
+  wave_lds_sync();
+
+  bool avail[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    avail[i] = e < E;
+    if (avail[i] && !sl.keep[e / epg]) b[i] = -INFINITY;  // excluded group
+  }
+  for (int k = 0; k < K; ++k) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (avail[i] && better(b[i], e, bv, bi)) {
+        bv = b[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    // bi < E always: at least K >= 1 available experts remain (K <= E)
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (bi == lane + 64 * i) avail[i] = false;
+    if (lane == 0) {
+      sl.sel[k] = sl.score[bi];
+      if (live) st<COH>(idx_out + (size_t)t * K + k, (int32_t)bi);
+    }
+  }
+  wave_lds_sync();
+  if (lane < K && live) {
+    float sum = 0.f;
+    for (int k = 0; k < K; ++k) sum += sl.sel[k];
+    st<COH>(w_out + (size_t)t * K + lane, sl.sel[lane] / sum * route_scale);
+  }
+}
+
+}  // namespace
+
+}  // namespace moe

@@ -75,6 +75,53 @@ hipError_t launch_combine_partial(const int32_t* idx, const float* w, const int3
                                   const uint16_t* rows, int has_shared, int T, int K, int e_lo, int e_hi, int d,
                                   float* y, hipStream_t s);
 
+// decode.hip: the whole layer in one launch for T <= DEC_MAX_TOKENS (e4m3
+// expert weights).  The control block (DEC_CTL_INTS ints at the start of the
+// workspace) must be zero before the first launch on it; every launch leaves
+// it zero except DEC_CTL_STATUS, which then holds 1 if a wait gave up (the
+// outputs are not valid) and 0 otherwise.
+constexpr int DEC_MAX_TOKENS = 64;
+enum : int {
+  DEC_CTL_QUANT = 0,    // quantisation items done
+  DEC_CTL_GATE = 1,     // router partial items done
+  DEC_CTL_SELECT = 2,   // selection items done
+  DEC_CTL_PLAN = 3,     // permutation + tile list done
+  DEC_CTL_DOWN = 4,     // down-projection items done
+  DEC_CTL_FINISHED = 5, // workgroups finished
+  DEC_CTL_STALLED = 6,  // a wait gave up
+  DEC_CTL_STATUS = 7,   // status of the last completed launch
+  DEC_CTL_UP = 8,       // DEC_CTL_UP + tile: up-projection items of that tile done
+};
+constexpr int DEC_CTL_INTS = 1024;
+
+struct DecodeShape {
+  int max_tiles, nsh, gate_kz, gate_kchunk, comb_parts;
+  int b_gate, b_sup, b_sel, b_plan, b_rup, b_down, b_comb, b_end;  // item ranges
+};
+DecodeShape decode_shape(int T, int d, int I, int E, int K);
+
+struct DecodeBufs {
+  int* ctl;
+  float* zpart;  // 2 gate_kz planes of [T][E]
+  int32_t* idx;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* row_token;
+  int32_t* pair_row;
+  int4* tiles;
+  int32_t* n_tiles;
+  uint8_t* xq;
+  float* xs;
+  uint8_t* hq;
+  float* hs;
+  uint16_t* rows;
+};
+hipError_t launch_decode(const DecodeShape& sh, const ExpertPtrs& routed, const ExpertPtrs& shared,
+                         const uint16_t* x, const float* gate_w, const float* gate_b, int T, int d, int I, int E,
+                         int G, int TG, int K, float route_scale, const DecodeBufs& bufs, uint16_t* delta,
+                         hipStream_t s);
+
 // norm.hip
 hipError_t launch_add_rmsnorm(const uint16_t* x, uint16_t* residual, const float* gain, float eps, int d,
                               int64_t T, uint16_t* out, hipStream_t s);

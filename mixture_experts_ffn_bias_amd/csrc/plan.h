@@ -6,34 +6,40 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace moe {
 
 // Thread e (0..255) brings expert e's permuted rows [lo, lo + cnt) (ignored
-// outside [e_lo, e_hi)); s is 256 ints of LDS.  Routed experts [e_lo, e_hi)
+// outside [e_lo, e_hi)); threads from 256 on only join the barriers.  s is
+// 256 ints of LDS.  Routed experts [e_lo, e_hi)
 // are numbered from e_lo; with has_shared the shared expert (number
 // e_hi - e_lo, rows [T*K, T*K + T)) is planned first.  once = 1 marks the
-// only tile of its expert.  At most cap routed tiles are written.
+// only tile of its expert.  At most cap routed tiles are written.  COH: the
+// list is written with agent-coherent stores (common.h, ld / st).
+template <bool COH = false>
 __device__ __forceinline__ void plan_tiles_block(int lo, int cnt, int T, int K, int NT, int has_shared, int cap,
                                                  int e_lo, int e_hi, int* s, int4* __restrict__ tiles,
                                                  int32_t* __restrict__ n_tiles) {
   const int e = threadIdx.x;
+  const bool act = e < 256;
   const int TK = T * K;
   const int nsh = has_shared ? (T + NT - 1) / NT : 0;
   for (int j = threadIdx.x; j < nsh; j += blockDim.x)
-    tiles[j] = make_int4(e_hi - e_lo, TK + j * NT, min(NT, T - j * NT), nsh == 1 ? 1 : 0);
-  const int n = (e >= e_lo && e < e_hi) ? (cnt + NT - 1) / NT : 0;
-  s[e] = n;
+    st16<COH>(tiles + j, make_uint4(e_hi - e_lo, TK + j * NT, min(NT, T - j * NT), nsh == 1 ? 1 : 0));
+  const int n = (act && e >= e_lo && e < e_hi) ? (cnt + NT - 1) / NT : 0;
+  if (act) s[e] = n;
   __syncthreads();
   for (int o = 1; o < 256; o <<= 1) {
-    const int v = e >= o ? s[e - o] : 0;
+    const int v = act && e >= o ? s[e - o] : 0;
     __syncthreads();
-    s[e] += v;
+    if (act) s[e] += v;
     __syncthreads();
   }
-  const int base = s[e] - n;
+  const int base = act ? s[e] - n : 0;
   for (int j = 0; j < n && base + j < cap; ++j)
-    tiles[nsh + base + j] = make_int4(e - e_lo, lo + j * NT, min(NT, cnt - j * NT), n == 1 ? 1 : 0);
-  if (threadIdx.x == 0) *n_tiles = nsh + min(s[255], cap);
+    st16<COH>(tiles + nsh + base + j, make_uint4(e - e_lo, lo + j * NT, min(NT, cnt - j * NT), n == 1 ? 1 : 0));
+  if (threadIdx.x == 0) st<COH>(n_tiles, (int32_t)(nsh + min(s[255], cap)));
 }
 
 }  // namespace moe

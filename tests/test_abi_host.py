@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     assert moe.status_string(0) == "ok"
-    for c in (-1, -2, -3, -4, -5):
+    for c in (-1, -2, -3, -4, -5, -6):
         assert moe.status_string(c) not in ("ok", "unknown status")
 
 
@@ -201,3 +201,38 @@ def test_shard_argument_checks():
     assert call(0, 32, 1, ws=0) == -3
     noshared = moe.moe_weights(FAKE, FAKE, ex, moe.moe_experts(None, None, None, None, None, None))
     assert call(0, 32, 1, wt=ctypes.byref(noshared)) == -1   # the shared expert is required with with_shared
+
+
+def test_fused_workspace_sizes():
+    d = dims()
+    assert moe.moe_forward_fused_workspace_size(d, 0) == 0
+    assert moe.moe_forward_fused_workspace_size(d, 65) == 0          # single launch: at most 64 tokens
+    assert moe.moe_forward_fused_workspace_size(d, -1) == 0
+    small, full = moe.moe_forward_fused_workspace_size(d, 1), moe.moe_forward_fused_workspace_size(d, 64)
+    assert 4096 < small < full
+    assert full > 64 * 7168 * 9 * 2                                   # the bf16 expert-output rows
+    assert moe.moe_forward_fused_workspace_size(dims(d_model=7000), 8) == 0
+
+
+def test_fused_argument_checks():
+    L = B.lib()
+    d = ctypes.byref(dims())
+    ex = moe.moe_experts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    w = moe.moe_weights(FAKE, FAKE, ex, ex)
+    need = moe.moe_forward_fused_workspace_size(dims(), 16)
+    call = lambda T=16, wt=ctypes.byref(w), x=FAKE, out=FAKE, ws=FAKE, n=need: L.moe_forward_fused(
+        d, wt, T, x, out, None, None, ws, n, None)
+    assert call(T=0) == 0                # no tokens: no-op
+    assert call(T=65) == -2              # beyond the single-launch batch
+    assert call(T=-1) == -1
+    assert call(wt=None) == -1
+    assert call(x=None) == -1
+    assert call(out=FAKE + 2) == -4
+    assert call(ws=FAKE + 64) == -4
+    assert call(n=need - 1) == -3
+    assert call(ws=None) == -3
+    nobias = moe.moe_weights(FAKE, None, ex, ex)
+    assert call(wt=ctypes.byref(nobias)) == -1
+    noshared = moe.moe_weights(FAKE, FAKE, ex, moe.moe_experts(None, None, None, None, None, None))
+    assert call(wt=ctypes.byref(noshared)) == -1
+    assert L.moe_forward_fused_status(None, None) == -1
