@@ -16,13 +16,17 @@
 // rather than after the whole up-projection.
 //
 // Completion counts live in a control block at the start of the workspace.
-// Everything one item hands to another is written and read with
-// agent-coherent accesses (common.h, ld / st; the activation copies of the
-// FFN with the matching cache policy), so no L2 writeback or invalidation is
-// needed (per workgroup, those cost the FFN a third of its bandwidth): a
-// producer's waves wait until their stores have completed, then one thread
-// bumps the count; a consumer's first thread polls it and the workgroup
-// barrier releases the other threads, whose loads come after.  The waits
+// Everything one item hands to another is written with agent-coherent stores
+// (common.h, ld / st: through to the memory all XCDs share), so no L2
+// writeback or invalidation is needed (per workgroup, those cost the FFN a
+// third of its bandwidth): a producer's waves wait until their stores have
+// completed, then one thread bumps the count; a consumer's first thread polls
+// it and the workgroup barrier releases the other threads, whose loads come
+// after.  A consumer may read through its L2 (which holds nothing of the
+// workspace at launch) because every cache line it reads is complete before
+// any workgroup reads it, with one exception: a line of the FFN's activation
+// scales spans rows of tiles that finish at different times, so those are
+// copied with agent-coherent loads.  The waits
 // are bounded: a workgroup that has polled too long marks the call as
 // stalled and skips its work (the result is then garbage and the status
 // word says so), so the launch always ends.  Since workgroups are handed out
@@ -65,12 +69,17 @@ struct DecodeArgs {
   int b_gate, b_sup, b_sel, b_plan, b_rup, b_down, b_comb, b_end;
 };
 
-// Poll (thread 0) until ctl[i] >= target; then every thread may read, with
-// agent-coherent loads, what the counted items wrote.  False when the call
-// has stalled.
+// Poll (thread 0) until ctl[i] >= target; then every thread may read what
+// the counted items wrote.  False when the call has stalled.  The first look
+// goes through the XCD's L2: a count only grows during a launch and the L2
+// holds none at launch, so a cached value can only be short, never early;
+// once a count is complete, the other workgroups of the XCD that wait for it
+// see so without a round trip to memory.  Otherwise the count is polled
+// with agent-coherent loads.
 __device__ bool dec_wait(int* ctl, int i, int target, int* s_ok) {
   if (threadIdx.x == 0) {
     int ok = 1;
+    if (__hip_atomic_load(ctl + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target)
     for (int n = 0;; ++n) {
       if (__hip_atomic_load(ctl + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) break;
       if (__hip_atomic_load(ctl + DEC_CTL_STALLED, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0 ||
@@ -98,10 +107,10 @@ __device__ void dec_signal(int* ctl, int i) {
   if (threadIdx.x == 0) __hip_atomic_fetch_add(ctl + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Entry `tile` of the tile list (agent-coherent).
-__device__ int4 tile_desc(const FfnArgs& f, int tile) {
-  const uint4 v = ld16<true>(f.tiles + tile);
-  return make_int4((int)v.x, (int)v.y, (int)v.z, (int)v.w);
+// Tile-list entry of the shared expert's tile j (as the plan writes it).
+__device__ int4 shared_tile(const DecodeArgs& a, int j) {
+  const FfnArgs& f = a.f;
+  return make_int4(f.E, f.T * f.K + j * DEC_ROWS, min(DEC_ROWS, f.T - j * DEC_ROWS), a.nsh == 1 ? 1 : 0);
 }
 
 __device__ bool stalled(const int* ctl) {
@@ -142,9 +151,8 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_kernel(DecodeArgs a) {
     const int i = b - a.b_sup;
     const int j = i / nib;
     if (dec_wait(ctl, DEC_CTL_QUANT, a.b_gate, &s_ok)) {
-      const int4 td = make_int4(E, T * K + j * DEC_ROWS, min(DEC_ROWS, T - j * DEC_ROWS), a.nsh == 1 ? 1 : 0);
       Item<DEC_ROWS> it;
-      up_item_of<DEC_ROWS, false, true>(f, td, i - j * nib, it);
+      up_item_of<DEC_ROWS, false>(f, shared_tile(a, j), i - j * nib, it);
       ffn_run_item<true, DEC_ROWS, false, true>(f, it, smem);
     }
     dec_signal(ctl, DEC_CTL_UP + j);
@@ -156,7 +164,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_kernel(DecodeArgs a) {
       GateSlot* slots = reinterpret_cast<GateSlot*>(smem);
       GateSlot& sl = slots[threadIdx.x >> 6];
       const int tt = min(nsel_tok, T - 1);
-      gate_scores_wave<true>(a.zpart, 2 * a.gate_kz, a.gate_b, T, E, tt, sl);
+      gate_scores_wave(a.zpart, 2 * a.gate_kz, a.gate_b, T, E, tt, sl);
       gate_choose_wave<true>(sl, E, a.G, a.TG, K, a.route_scale, nsel_tok, nsel_tok < T, a.idx, a.w);
     }
     dec_signal(ctl, DEC_CTL_SELECT);
@@ -165,39 +173,51 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_kernel(DecodeArgs a) {
     if (dec_wait(ctl, DEC_CTL_SELECT, a.b_plan - a.b_sel, &s_ok)) {
       const PlanArgs plan{const_cast<int4*>(f.tiles), const_cast<int32_t*>(f.n_tiles), DEC_ROWS, 1, a.cap};
       permute_block<true>(a.idx, T, K, E, a.counts, a.offsets, const_cast<int32_t*>(f.row_token), a.pair_row, plan,
-                          *reinterpret_cast<PermLds*>(smem));
+                          *reinterpret_cast<PermLds*>(smem));  // (its few loads of idx are agent-coherent too)
+      // Tiles past the end of the list count as up-projected (once the list
+      // is in memory), so a down-projection item needs to wait for its own
+      // tile's count only, and then finds out from the list whether it has
+      // work.
+      asm volatile("" ::: "memory");
+      wait_vmcnt<0>();
+      __syncthreads();
+      for (int t = ld<true>(f.n_tiles) + threadIdx.x; t < a.max_tiles; t += DEC_THREADS)
+        __hip_atomic_store(ctl + DEC_CTL_UP + t, nib, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     dec_signal(ctl, DEC_CTL_PLAN);
   } else if (b < a.b_down) {
     // routed up-projection: tiles nsh.. of the list
     const int r = b - a.b_rup;
     const int tile = a.nsh + r / nib;
-    if (dec_wait(ctl, DEC_CTL_PLAN, 1, &s_ok) && tile < ld<true>(f.n_tiles)) {
+    if (dec_wait(ctl, DEC_CTL_PLAN, 1, &s_ok) && tile < *f.n_tiles) {
       Item<DEC_ROWS> it;
-      up_item_of<DEC_ROWS, false, true>(f, tile_desc(f, tile), r - (r / nib) * nib, it);
+      up_item_of<DEC_ROWS, false>(f, f.tiles[tile], r - (r / nib) * nib, it);
       ffn_run_item<true, DEC_ROWS, false, true>(f, it, smem);
       dec_signal(ctl, DEC_CTL_UP + tile);
     }
   } else if (b < a.b_comb) {
     // down-projection of tile dn / nob2 once its up-projection is complete
+    // (for a routed tile that also means the tile list is in memory; a
+    // shared tile's entry is known without it)
     const int dn = b - a.b_down;
     const int tile = dn / nob2;
-    if (dec_wait(ctl, DEC_CTL_PLAN, 1, &s_ok) && tile < ld<true>(f.n_tiles)) {
-      if (dec_wait(ctl, DEC_CTL_UP + tile, nib, &s_ok)) {
+    if (dec_wait(ctl, DEC_CTL_UP + tile, nib, &s_ok)) {
+      const bool sh = tile < a.nsh;
+      if (sh || tile < *f.n_tiles) {
         Item<DEC_ROWS> it;
-        down_item_of<DEC_ROWS, false>(f, tile_desc(f, tile), dn - tile * nob2, it);
+        down_item_of<DEC_ROWS, false>(f, sh ? shared_tile(a, tile) : f.tiles[tile], dn - tile * nob2, it);
         ffn_run_item<false, DEC_ROWS, false, true>(f, it, smem);
+        dec_signal(ctl, DEC_CTL_DOWN);
       }
-      dec_signal(ctl, DEC_CTL_DOWN);
     }
   } else {
     // combine: token c / parts, share c % parts of its row, after every down item
     const int c = b - a.b_comb;
     const int t = c / a.comb_parts;
     if (dec_wait(ctl, DEC_CTL_PLAN, 1, &s_ok)) {
-      const int n_down = ld<true>(f.n_tiles) * nob2;
+      const int n_down = *f.n_tiles * nob2;
       if (dec_wait(ctl, DEC_CTL_DOWN, n_down, &s_ok))
-        combine_token<false, true>(a.idx, a.w, a.pair_row, f.out, 1, T, K, 0, E, d, a.delta, t, c - t * a.comb_parts,
+        combine_token<false>(a.idx, a.w, a.pair_row, f.out, 1, T, K, 0, E, d, a.delta, t, c - t * a.comb_parts,
                              a.comb_parts, *reinterpret_cast<CombineLds*>(smem));
     }
   }

@@ -113,8 +113,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 // pieces [APW w, APW w + APW) (waves w < AWAVES) and, e4m3 only, for
 // w < SWAVES the scales of activation rows [64w, 64w + 64).  Lane l of a
 // piece covers row piece_row0 + l/8 and LDS slot l%8, so it fetches global
-// chunk (l%8) ^ swz(row).  WPOL / APOL: cache policy of the weight and of the
-// activation (and scale) copies.
+// chunk (l%8) ^ swz(row).  WPOL / SPOL: cache policy of the weight and of the
+// activation-scale copies.
 template <int ROWS>
 struct TileSrc {
   const uint8_t* a[4];                // this lane's source rows for the four weight pieces (chunk applied)
@@ -130,7 +130,7 @@ __device__ __forceinline__ int tile_copies(int wave, bool act) {
   return 4 + (act ? G::APW : 0) + (!BF && wave < G::SWAVES ? 1 : 0);
 }
 
-template <int ROWS, bool BF, int WPOL, int APOL>
+template <int ROWS, bool BF, int WPOL, int SPOL>
 __device__ __forceinline__ void tile_issue(const TileSrc<ROWS>& src, uint8_t* stage, int kb, int wave, bool act) {
   using G = Tile<ROWS>;
   const int off = kb * BLK;
@@ -142,12 +142,12 @@ __device__ __forceinline__ void tile_issue(const TileSrc<ROWS>& src, uint8_t* st
 #pragma unroll
     for (int j = 0; j < G::APW; ++j)
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.b[j] + off),
-                                       (lds_ptr_t)(stage + TT_A_BYTES + (wave * G::APW + j) * 1024), 16, 0, APOL);
+                                       (lds_ptr_t)(stage + TT_A_BYTES + (wave * G::APW + j) * 1024), 16, 0, 0);
   }
   if (!BF && wave < G::SWAVES) {
     if (ROWS >= 64 || (threadIdx.x & 63) < ROWS)
       __builtin_amdgcn_global_load_lds((gbl_ptr_t)(src.s + kb),
-                                       (lds_ptr_t)(stage + TT_A_BYTES + G::B_BYTES + wave * 256), 4, 0, APOL);
+                                       (lds_ptr_t)(stage + TT_A_BYTES + G::B_BYTES + wave * 256), 4, 0, SPOL);
   }
 }
 
@@ -259,7 +259,7 @@ __device__ __forceinline__ void kblock_multiply(const uint8_t* stage, const_f32_
 // (0..4; a compile-time count keeps the K-block body free of branches, so the
 // LDS reads, decodes and MFMAs of a block can be interleaved).  WPOL: cache
 // policy of the weight copies.
-template <int ROWS, bool BF, int MV, int WPOL, int APOL>
+template <int ROWS, bool BF, int MV, int WPOL, int SPOL>
 __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS>& src, const_f32_ptr sa0,
                                                const_f32_ptr sa1, int nkb, int nrows,
                                                v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
@@ -273,7 +273,7 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS
 #pragma unroll
   for (int k = 0; k < AHEAD; ++k) {
     if (k < nkb) {
-      tile_issue<ROWS, BF, WPOL, APOL>(src, smem + k * G::STAGE, k, wave, act);
+      tile_issue<ROWS, BF, WPOL, SPOL>(src, smem + k * G::STAGE, k, wave, act);
       ++issued;
     }
   }
@@ -288,7 +288,7 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS
   for (int kb = 0; kb < nkb; ++kb) {
     if (kb + AHEAD < nkb) {
       const int nb = cur == 0 ? G::NSTAGE - 1 : cur - 1;  // (kb + AHEAD) % NSTAGE
-      tile_issue<ROWS, BF, WPOL, APOL>(src, smem + nb * G::STAGE, kb + AHEAD, wave, act);
+      tile_issue<ROWS, BF, WPOL, SPOL>(src, smem + nb * G::STAGE, kb + AHEAD, wave, act);
     }
     // a wave whose 64 rows hold no tile row (MV = 0) only helps with the copies
     kblock_multiply<ROWS, BF, MV>(smem + cur * G::STAGE, sa0, sa1, kb, acc);
@@ -298,23 +298,23 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS
   }
 }
 
-template <int ROWS, bool BF, int WPOL, int APOL>
+template <int ROWS, bool BF, int WPOL, int SPOL>
 __device__ __forceinline__ void run_mainloop_pol(uint8_t* smem, const TileSrc<ROWS>& src, const_f32_ptr c0,
                                                  const_f32_ptr c1, int nkb, int nrows, int mvalid,
                                                  v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
   if constexpr (Tile<ROWS>::MVMAX == 4) {
     switch (mvalid) {
-      case 0: tiled_mainloop<ROWS, BF, 0, WPOL, APOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      case 1: tiled_mainloop<ROWS, BF, 1, WPOL, APOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      case 2: tiled_mainloop<ROWS, BF, 2, WPOL, APOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      case 3: tiled_mainloop<ROWS, BF, 3, WPOL, APOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      default: tiled_mainloop<ROWS, BF, 4, WPOL, APOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 0: tiled_mainloop<ROWS, BF, 0, WPOL, SPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 1: tiled_mainloop<ROWS, BF, 1, WPOL, SPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 2: tiled_mainloop<ROWS, BF, 2, WPOL, SPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 3: tiled_mainloop<ROWS, BF, 3, WPOL, SPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      default: tiled_mainloop<ROWS, BF, 4, WPOL, SPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
     }
   } else {
     switch (mvalid) {
-      case 0: tiled_mainloop<ROWS, BF, 0, WPOL, APOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      case 1: tiled_mainloop<ROWS, BF, 1, WPOL, APOL>(smem, src, c0, c1, nkb, nrows, acc); break;
-      default: tiled_mainloop<ROWS, BF, 2, WPOL, APOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 0: tiled_mainloop<ROWS, BF, 0, WPOL, SPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      case 1: tiled_mainloop<ROWS, BF, 1, WPOL, SPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
+      default: tiled_mainloop<ROWS, BF, 2, WPOL, SPOL>(smem, src, c0, c1, nkb, nrows, acc); break;
     }
   }
 }
@@ -322,15 +322,15 @@ __device__ __forceinline__ void run_mainloop_pol(uint8_t* smem, const TileSrc<RO
 // The main loop for this tile (mvalid: wave-uniform count of this wave's
 // 16-row sub-tiles that hold rows), with non-temporal weight copies when the
 // tile reads them once.
-template <int ROWS, bool BF, int APOL>
+template <int ROWS, bool BF, int SPOL>
 __device__ __forceinline__ void run_mainloop(uint8_t* smem, const TileSrc<ROWS>& src, const float* sa0,
                                              const float* sa1, int nkb, int nrows, int mvalid, bool once,
                                              v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
   const const_f32_ptr c0 = (const_f32_ptr)sa0, c1 = (const_f32_ptr)sa1;
   if (once)
-    run_mainloop_pol<ROWS, BF, CPOL_NT, APOL>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
+    run_mainloop_pol<ROWS, BF, CPOL_NT, SPOL>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
   else
-    run_mainloop_pol<ROWS, BF, 0, APOL>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
+    run_mainloop_pol<ROWS, BF, 0, SPOL>(smem, src, c0, c1, nkb, nrows, mvalid, acc);
 }
 
 // DMA source pointers of this lane.  wrow(i): weight row of tile row i
@@ -581,10 +581,14 @@ __device__ __forceinline__ void zero_acc(v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
 }
 
 // All K blocks and the epilogue of one item; smem: Tile<ROWS>::SMEM bytes of
-// LDS.  Called by every thread of a 512-thread workgroup.  COH: activations
-// and their scales are copied with agent-coherent loads and the outputs
-// written with agent-coherent stores (common.h, ld / st); the weights, which
-// no kernel writes, keep their cache policy.
+// LDS.  Called by every thread of a 512-thread workgroup.  COH (for the
+// single-launch layer kernel, where other workgroups of the same launch
+// produce the activations and consume the outputs): the outputs are written
+// with agent-coherent stores and the activation scales copied with
+// agent-coherent loads (common.h, ld / st).  Activation rows keep the plain
+// policy: every 128-byte line of them comes from one producer, complete
+// before any workgroup reads it; a line of scales spans two rows, which may
+// belong to tiles finished at different times.
 template <bool UP, int ROWS, bool BF, bool COH = false>
 __device__ __forceinline__ void ffn_run_item(const FfnArgs& a, const Item<ROWS>& it, uint8_t* smem) {
   constexpr int EB = BF ? 2 : 1;
