@@ -88,7 +88,10 @@ __device__ bool dec_wait(int* ctl, int i, int target, int* s_ok) {
         ok = 0;
         break;
       }
-      __builtin_amdgcn_s_sleep(4);
+      if (n < 8)  // back off: long waits poll less
+        __builtin_amdgcn_s_sleep(2);
+      else
+        __builtin_amdgcn_s_sleep(16);
     }
     *s_ok = ok;
   }
@@ -111,6 +114,21 @@ __device__ void dec_signal(int* ctl, int i) {
 __device__ int4 shared_tile(const DecodeArgs& a, int j) {
   const FfnArgs& f = a.f;
   return make_int4(f.E, f.T * f.K + j * DEC_ROWS, min(DEC_ROWS, f.T - j * DEC_ROWS), a.nsh == 1 ? 1 : 0);
+}
+
+// The next item of a range from its counter (every workgroup of the range
+// takes one, so the items handed out are exactly the range's).  Items taken
+// this way still only wait for items of earlier ranges, all of whose
+// workgroups each dispatcher starts before any of this range.  (Measured:
+// worth it for the short down-projection items, where the XCDs' different
+// rates leave a tail; not for the up-projection, whose tail the
+// down-projection fills.)
+__device__ int take_ticket(int* ctl, int i, int* s) {
+  if (threadIdx.x == 0) *s = __hip_atomic_fetch_add(ctl + i, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int t = *s;
+  __syncthreads();
+  return t;
 }
 
 __device__ bool stalled(const int* ctl) {
@@ -199,7 +217,10 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_kernel(DecodeArgs a) {
     // down-projection of tile dn / nob2 once its up-projection is complete
     // (for a routed tile that also means the tile list is in memory; a
     // shared tile's entry is known without it)
-    const int dn = b - a.b_down;
+    // The item is taken from a counter rather than from the workgroup index:
+    // the XCDs (each gets every eighth workgroup) stream at different rates,
+    // and the faster ones then take more of the items.
+    const int dn = take_ticket(ctl, DEC_CTL_DTICKET, &s_ok);
     const int tile = dn / nob2;
     if (dec_wait(ctl, DEC_CTL_UP + tile, nib, &s_ok)) {
       const bool sh = tile < a.nsh;
@@ -228,8 +249,10 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_kernel(DecodeArgs a) {
     const int done = __hip_atomic_fetch_add(ctl + DEC_CTL_FINISHED, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (done == (int)gridDim.x - 1) {
       const int st = stalled(ctl) ? 1 : 0;
-      for (int i = 0; i < DEC_CTL_UP + a.max_tiles; ++i)
+      for (int i = 0; i < DEC_CTL_UP; i += 32)
         if (i != DEC_CTL_STATUS) __hip_atomic_store(ctl + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = DEC_CTL_UP; i < DEC_CTL_UP + a.max_tiles; ++i)
+        __hip_atomic_store(ctl + i, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(ctl + DEC_CTL_STATUS, st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }

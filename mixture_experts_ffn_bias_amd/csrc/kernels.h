@@ -81,16 +81,19 @@ hipError_t launch_combine_partial(const int32_t* idx, const float* w, const int3
 // it zero except DEC_CTL_STATUS, which then holds 1 if a wait gave up (the
 // outputs are not valid) and 0 otherwise.
 constexpr int DEC_MAX_TOKENS = 64;
+// Control words, each count in a cache line of its own (many workgroups poll
+// some of them while others add to them).
 enum : int {
-  DEC_CTL_QUANT = 0,    // quantisation items done
-  DEC_CTL_GATE = 1,     // router partial items done
-  DEC_CTL_SELECT = 2,   // selection items done
-  DEC_CTL_PLAN = 3,     // permutation + tile list done
-  DEC_CTL_DOWN = 4,     // down-projection items done
-  DEC_CTL_FINISHED = 5, // workgroups finished
-  DEC_CTL_STALLED = 6,  // a wait gave up
-  DEC_CTL_STATUS = 7,   // status of the last completed launch
-  DEC_CTL_UP = 8,       // DEC_CTL_UP + tile: up-projection items of that tile done
+  DEC_CTL_QUANT = 0,      // quantisation items done
+  DEC_CTL_GATE = 32,      // router partial items done
+  DEC_CTL_SELECT = 64,    // selection items done
+  DEC_CTL_PLAN = 96,      // permutation + tile list done
+  DEC_CTL_DOWN = 128,     // down-projection items done
+  DEC_CTL_FINISHED = 160, // workgroups finished
+  DEC_CTL_STALLED = 192,  // a wait gave up
+  DEC_CTL_STATUS = 224,   // status of the last completed launch
+  DEC_CTL_DTICKET = 256,  // down-projection items handed out
+  DEC_CTL_UP = 288,       // DEC_CTL_UP + tile: up-projection items of that tile done
 };
 constexpr int DEC_CTL_INTS = 1024;
 
