@@ -161,7 +161,7 @@ __global__ __launch_bounds__(DEC_THREADS, 4) void decode_kernel(DecodeArgs a) {
     const int hk = a.gate_kchunk / 2;
     const int k0 = min(d, z * a.gate_kchunk + half * hk), k1 = min(d, k0 + hk);
     if (t0 < T)
-      gate_logits_wave<true>(a.x, a.gate_w, a.zpart + (size_t)(2 * z + half) * T * E, T, d, E, t0, 16 * et, 1, k0,
+      gate_logits_wave<1, true>(a.x, a.gate_w, a.zpart + (size_t)(2 * z + half) * T * E, T, d, E, t0, 16 * et, 1, k0,
                              k1);
     dec_signal(ctl, DEC_CTL_GATE);
   } else if (b < a.b_sel) {

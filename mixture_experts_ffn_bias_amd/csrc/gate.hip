@@ -10,20 +10,21 @@ namespace {
 
 constexpr int GATE_KSPLIT_MAX = 16;  // K splits of the logits (partials the selection adds)
 
-// Grid (ceil(T/64), ceil(E/(16 ntw)), ksplit), 256 threads.  Wave w owns
-// tokens [t0, t0+16) and up to ntw (1..4) 16-expert tiles; blockIdx.z a K
+// Grid (ceil(T/64), ceil(E/(16 NTW)), ksplit), 256 threads.  Wave w owns
+// tokens [t0, t0+16) and up to NTW (1 or 4) 16-expert tiles; blockIdx.z a K
 // range.  zpart[z][t][e] receives the partial logits of that K range.
+template <int NTW>
 __global__ __launch_bounds__(256) void gate_logits_kernel(const uint16_t* __restrict__ x,
                                                           const float* __restrict__ gw,
                                                           float* __restrict__ zpart, int T, int d, int E,
-                                                          int kchunk, int ntw) {
+                                                          int kchunk) {
   const int wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * 64 + wave * 16;
-  const int e0 = blockIdx.y * 16 * ntw;
+  const int e0 = blockIdx.y * 16 * NTW;
   const int k0 = blockIdx.z * kchunk;
   if (t0 >= T) return;  // no barriers in this kernel
-  gate_logits_wave(x, gw, zpart + (size_t)blockIdx.z * T * E, T, d, E, t0, e0, min(ntw, (E - e0) >> 4), k0,
-                   min(d, k0 + kchunk));
+  gate_logits_wave<NTW>(x, gw, zpart + (size_t)blockIdx.z * T * E, T, d, E, t0, e0, min(NTW, (E - e0) >> 4), k0,
+                        min(d, k0 + kchunk));
 }
 
 // WIDE = false: one wave per token, 4 tokens per 256-thread block; lane l
@@ -97,7 +98,10 @@ hipError_t launch_gate(const uint16_t* x, const float* gate_w, const float* gate
   const int kz = (d + kchunk - 1) / kchunk;
   const int ntw = gate_tiles_per_wave(T);
   dim3 grid((T + 63) / 64, (E + 16 * ntw - 1) / (16 * ntw), kz);
-  hipLaunchKernelGGL(gate_logits_kernel, grid, dim3(256), 0, s, x, gate_w, zpart, T, d, E, kchunk, ntw);
+  if (ntw == 1)
+    hipLaunchKernelGGL(gate_logits_kernel<1>, grid, dim3(256), 0, s, x, gate_w, zpart, T, d, E, kchunk);
+  else
+    hipLaunchKernelGGL(gate_logits_kernel<4>, grid, dim3(256), 0, s, x, gate_w, zpart, T, d, E, kchunk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (kz >= 8 && T <= 1024)

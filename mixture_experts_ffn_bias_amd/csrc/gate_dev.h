@@ -28,48 +28,72 @@ __device__ __forceinline__ void split3(float w, __bf16& hi, __bf16& mid, __bf16&
 }
 
 // One wave: partial logits of tokens [t0, t0 + 16) (t0 < T; rows past T
-// repeat row T - 1 and are not stored) and nt (1..4) 16-expert tiles from e0,
-// over K range [k0, k1) (multiples of 32).  zp[t][e] (E columns) receives
-// the partial sums of this K range (COH: agent-coherent stores).
-template <bool COH = false>
+// repeat row T - 1 and are not stored) and nt (1..NTW) 16-expert tiles from
+// e0, over K range [k0, k1) (multiples of 32).  zp[t][e] (E columns)
+// receives the partial sums of this K range (COH: agent-coherent stores).
+// The loads of 4 / NTW K steps are issued before any of them is multiplied
+// (the loop is latency-bound otherwise); the products are accumulated in K
+// order all the same.
+template <int NTW, bool COH = false>
 __device__ __forceinline__ void gate_logits_wave(const uint16_t* __restrict__ x, const float* __restrict__ gw,
                                                  float* __restrict__ zp, int T, int d, int E, int t0, int e0,
                                                  int nt, int k0, int k1) {
+  static_assert(NTW == 1 || NTW == 2 || NTW == 4, "expert tiles per wave");
+  constexpr int U = 4 / NTW;  // K steps in flight
   const int lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const uint16_t* xr = x + (size_t)min(t0 + r, T - 1) * d;
-  const float* wr[4];
+  const float* wr[NTW];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) wr[n] = gw + (size_t)(e0 + 16 * min(n, nt - 1) + r) * d;
+  for (int n = 0; n < NTW; ++n) wr[n] = gw + (size_t)(e0 + 16 * min(n, nt - 1) + r) * d;
 
-  v4f acc[4];
+  v4f acc[NTW];
 #pragma unroll
-  for (int n = 0; n < 4; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int n = 0; n < NTW; ++n) acc[n] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  for (int k = k0; k < k1; k += 32) {
-    const v8bf a = *(const v8bf*)(xr + k + 8 * g);
+  for (int k = k0; k < k1; k += 32 * U) {
+    v8bf a[U];
+    float4 f0[U][NTW], f1[U][NTW];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      if (n < nt) {
-        const float4 f0 = *(const float4*)(wr[n] + k + 8 * g);
-        const float4 f1 = *(const float4*)(wr[n] + k + 8 * g + 4);
-        const float f[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-        v8bf hi, mid, lo;
+    for (int u = 0; u < U; ++u) {
+      if (k + 32 * u < k1) {
+        const int kk = k + 32 * u + 8 * g;
+        a[u] = *(const v8bf*)(xr + kk);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          __bf16 h, m, l;
-          split3(f[j], h, m, l);
-          hi[j] = h;
-          mid[j] = m;
-          lo[j] = l;
+        for (int n = 0; n < NTW; ++n) {
+          if (n < nt) {
+            f0[u][n] = *(const float4*)(wr[n] + kk);
+            f1[u][n] = *(const float4*)(wr[n] + kk + 4);
+          }
         }
-        acc[n] = mfma_bf16(a, lo, acc[n]);
-        acc[n] = mfma_bf16(a, mid, acc[n]);
-        acc[n] = mfma_bf16(a, hi, acc[n]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (k + 32 * u < k1) {
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) {
+          if (n < nt) {
+            const float f[8] = {f0[u][n].x, f0[u][n].y, f0[u][n].z, f0[u][n].w,
+                                f1[u][n].x, f1[u][n].y, f1[u][n].z, f1[u][n].w};
+            v8bf hi, mid, lo;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              __bf16 h, m, l;
+              split3(f[j], h, m, l);
+              hi[j] = h;
+              mid[j] = m;
+              lo[j] = l;
+            }
+            acc[n] = mfma_bf16(a[u], lo, acc[n]);
+            acc[n] = mfma_bf16(a[u], mid, acc[n]);
+            acc[n] = mfma_bf16(a[u], hi, acc[n]);
+          }
+        }
       }
     }
   }
 #pragma unroll
-  for (int n = 0; n < 4; ++n) {
+  for (int n = 0; n < NTW; ++n) {
     if (n < nt) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
