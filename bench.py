@@ -75,7 +75,7 @@ class HipEvents:
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ("mixture_experts_ffn_bias_amd/csrc/ffn.hip", "mixture_experts_ffn_bias_amd/csrc/common.h")
+KERNEL_SOURCES = tuple("mixture_experts_ffn_bias_amd/csrc/" + f for f in ("ffn.hip", "ffn_tile.h", "plan.h", "common.h"))
 
 
 def kernel_source_digest() -> str:
