@@ -167,8 +167,22 @@ __device__ __forceinline__ void gate_scores_wave(const float* __restrict__ zpart
   }
 }
 
-__device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
-  return v > bv || (v == bv && i < bi);
+// Largest v over the 64 lanes of the wave, in every lane.  Data-parallel
+// (DPP) moves of the GFX9 family: max with the lane 1, 2, 4 and 8 places
+// lower in the same 16-lane row (lane 15 of a row then holds the row's
+// maximum), row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and
+// 3 (lane 63 then holds the wave's maximum), and lane 63 read out.  Lanes a
+// move has no source for take -inf.
+__device__ __forceinline__ float wave_max_dpp(float v) {
+  const int ninf = __float_as_int(-INFINITY);
+  int x = __float_as_int(v);
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x111, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x112, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x114, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x118, 0xf, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x142, 0xa, 0xf, false))));
+  x = __float_as_int(fmaxf(__int_as_float(x), __int_as_float(__builtin_amdgcn_update_dpp(ninf, x, 0x143, 0xc, 0xf, false))));
+  return __int_as_float(__builtin_amdgcn_readlane(x, 63));
 }
 
 // One wave, scores of token t in the slot: group score = sum of the two
@@ -177,6 +191,13 @@ __device__ __forceinline__ bool better(float v, int i, float bv, int bi) {
 // experts (ties to the lower expert).  Weights = chosen sigmoid scores
 // normalised to sum 1, times route_scale.  live: store idx and w of token t
 // (COH: with agent-coherent stores).
+//
+// Lane l holds experts l, l + 64, l + 128, l + 192 (E <= 256).  When the
+// group size divides 64 and is a power of two, a group is a segment of lanes
+// in one of those four sets, and its top two come from a butterfly over the
+// segment; otherwise lanes < G scan their group in LDS.  Each of the K picks
+// is a DPP wave maximum of the lanes' best available scores, and the lowest
+// expert index holding it comes from a ballot.
 template <bool COH = false>
 __device__ __forceinline__ void gate_choose_wave(GateSlot& sl, int E, int G, int TG, int K, float route_scale,
                                                  int t, bool live, int32_t* __restrict__ idx_out,
@@ -190,7 +211,33 @@ __device__ __forceinline__ void gate_choose_wave(GateSlot& sl, int E, int G, int
     const int e = lane + 64 * i;
     b[i] = e < E ? sl.biased[e] : -INFINITY;
   }
-  if (lane < G) {
+  if (epg <= 64 && (epg & (epg - 1)) == 0) {
+    float m1[4], m2[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      m1[i] = b[i];
+      m2[i] = -INFINITY;
+    }
+    for (int o = 1; o < epg; o <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a1 = __shfl_xor(m1[i], o), a2 = __shfl_xor(m2[i], o);
+        m2[i] = fmaxf(fminf(m1[i], a1), fmaxf(m2[i], a2));
+        m1[i] = fmaxf(m1[i], a1);
+      }
+    }
+    if ((lane & (epg - 1)) == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int g = (lane + 64 * i) / epg;
+        if (g < G) {
+          float gs = m1[i] + m2[i];
+          if (gs != gs) gs = -INFINITY;
+          sl.gs[g] = gs;
+        }
+      }
+    }
+  } else if (lane < G) {
     float m1 = -INFINITY, m2 = -INFINITY;
     for (int j = 0; j < epg; ++j) {
       const float v = sl.biased[lane * epg + j];
@@ -225,26 +272,18 @@ __device__ __forceinline__ void gate_choose_wave(GateSlot& sl, int E, int G, int
     if (avail[i] && !sl.keep[e / epg]) b[i] = -INFINITY;  // excluded group
   }
   for (int k = 0; k < K; ++k) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    float lv = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (avail[i] && better(b[i], e, bv, bi)) {
-        bv = b[i];
-        bi = e;
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      if (avail[i]) lv = fmaxf(lv, b[i]);
+    const float mx = wave_max_dpp(lv);
+    // the lowest available expert holding mx (one exists: K <= E)
+    int bi = 0;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
+    for (int i = 3; i >= 0; --i) {
+      const uint64_t m = __ballot(avail[i] && b[i] == mx);
+      if (m) bi = 64 * i + __builtin_ctzll(m);
     }
-    // bi < E always: at least K >= 1 available experts remain (K <= E)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (bi == lane + 64 * i) avail[i] = false;
