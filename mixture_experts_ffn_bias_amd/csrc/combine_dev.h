@@ -25,8 +25,7 @@ namespace {
 // PARTIAL: y (fp32) = the sum over choices with expert in [e_lo, e_hi), plus
 // the shared row when has_shared; otherwise delta (bf16) = bf16(full sum).
 // Token t, share `part` of `nparts` of the row (8-element chunks); called by
-// every thread of the workgroup (K <= 32 <= blockDim.x).  COH: the routing
-// and the rows are read with agent-coherent loads (common.h, ld / st).
+// every thread of the workgroup (K <= 32 <= blockDim.x).
 struct CombineLds {
   int row[32];
   float w[32];
@@ -34,7 +33,7 @@ struct CombineLds {
   int n;
 };
 
-template <bool PARTIAL, bool COH = false>
+template <bool PARTIAL>
 __device__ __forceinline__ void combine_token(const int32_t* __restrict__ idx, const float* __restrict__ w,
                                               const int32_t* __restrict__ pair_row,
                                               const uint16_t* __restrict__ rows, int has_shared, int T, int K,
@@ -52,11 +51,11 @@ __device__ __forceinline__ void combine_token(const int32_t* __restrict__ idx, c
   float wk = 0.f;
   bool in = false;
   if (me < K) {
-    e = ld<COH>(idx + (size_t)t * K + me);
+    e = idx[(size_t)t * K + me];
     in = e >= e_lo && e < e_hi;
-    row = ld<COH>(pair_row + (size_t)t * K + me);
+    row = pair_row[(size_t)t * K + me];
     row = row < 0 ? 0 : (row >= TK ? (int)(TK - 1) : row);
-    wk = ld<COH>(w + (size_t)t * K + me);
+    wk = w[(size_t)t * K + me];
     s_e[me] = in ? e : 0x7fffffff;
   }
   __syncthreads();
@@ -85,7 +84,7 @@ __device__ __forceinline__ void combine_token(const int32_t* __restrict__ idx, c
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.f;
     for (int k = 0; k < n; ++k) {
-      const uint4 v = ld16<COH>(rows + (size_t)s_row[k] * d + c * 8);
+      const uint4 v = *(const uint4*)(rows + (size_t)s_row[k] * d + c * 8);
       const float wk = s_w[k];
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -95,7 +94,7 @@ __device__ __forceinline__ void combine_token(const int32_t* __restrict__ idx, c
       }
     }
     if (has_shared) {
-      const uint4 v = ld16<COH>(rows + (size_t)(TK + t) * d + c * 8);
+      const uint4 v = *(const uint4*)(rows + (size_t)(TK + t) * d + c * 8);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

@@ -104,23 +104,13 @@ __device__ __forceinline__ void st(T* p, T v) {
     *p = v;
 }
 
-// 8 and 16 bytes (16-byte aligned for ld16 / st16); COH: as 8-byte halves.
+// 8 and 16 bytes (16-byte aligned for st16); COH: as 8-byte halves.
 template <bool COH>
 __device__ __forceinline__ void st8(void* p, uint2 v) {
   if constexpr (COH)
     st<true>((uint64_t*)p, __builtin_bit_cast(uint64_t, v));
   else
     *(uint2*)p = v;
-}
-
-template <bool COH>
-__device__ __forceinline__ uint4 ld16(const void* p) {
-  if constexpr (COH) {
-    const uint64_t lo = ld<true>((const uint64_t*)p), hi = ld<true>((const uint64_t*)p + 1);
-    return make_uint4((uint32_t)lo, (uint32_t)(lo >> 32), (uint32_t)hi, (uint32_t)(hi >> 32));
-  } else {
-    return *(const uint4*)p;
-  }
 }
 
 template <bool COH>

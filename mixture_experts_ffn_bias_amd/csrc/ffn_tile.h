@@ -17,10 +17,9 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 // token of permuted row `row` (NULL map: rows are tokens, as for a dense
 // MLP).  Rows from TK = T*K on are the shared expert's, one per token in
 // token order, so they need no lookup.
-template <bool COH = false>
 __device__ __forceinline__ int token_of(const int32_t* row_token, int row, int T, int TK) {
   if (!row_token) return row;
-  return row >= TK ? min(row - TK, T - 1) : clampi(ld<COH>(row_token + row), 0, T - 1);
+  return row >= TK ? min(row - TK, T - 1) : clampi(row_token[row], 0, T - 1);
 }
 
 // With e4m3 weights, xq/hq are e4m3 rows with block scales xs/hs; with bf16
@@ -380,7 +379,7 @@ struct Item {
 
 // Up-projection item of tile td (tile list entry: expert, first row, rows,
 // once) and h block ib.
-template <int ROWS, bool BF, bool COH = false>
+template <int ROWS, bool BF>
 __device__ __forceinline__ void up_item_of(const FfnArgs& a, int4 td, int ib, Item<ROWS>& it) {
   constexpr int EB = BF ? 2 : 1;
   const int nib = a.I / BLK, nkb = a.d * EB / BLK;
@@ -396,12 +395,12 @@ __device__ __forceinline__ void up_item_of(const FfnArgs& a, int4 td, int ib, It
         return base + (eo * a.I + ib * BLK + (row & 127)) * (size_t)a.d * EB;
       },
       [&](int row) {
-        const int tok = token_of<COH>(rt, row0 + min(row, nrows - 1), a.T, TK);
+        const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T, TK);
         return a.xq + (size_t)tok * a.d * EB;
       },
       [&](int row) -> const float* {
         if (BF) return nullptr;
-        const int tok = token_of<COH>(rt, row0 + min(row, nrows - 1), a.T, TK);
+        const int tok = token_of(rt, row0 + min(row, nrows - 1), a.T, TK);
         return a.xs + (size_t)tok * nkb;
       });
   it.sa0 = BF ? nullptr : P.s1 + (eo * nib + ib) * nkb;

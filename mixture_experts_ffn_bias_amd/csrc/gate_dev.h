@@ -134,8 +134,7 @@ __device__ __forceinline__ void gate_score(GateSlot& sl, const float* __restrict
 // One wave: the logits of token tt from ksplit partial planes (plane stride
 // T*E), added in split order with eight splits of the lane's four experts
 // (lane, lane + 64, lane + 128, lane + 192) loaded before they are added,
-// then the scores into the slot (COH: agent-coherent loads).
-template <bool COH = false>
+// then the scores into the slot.
 __device__ __forceinline__ void gate_scores_wave(const float* __restrict__ zpart, int ksplit,
                                                  const float* __restrict__ bias, int T, int E, int tt,
                                                  GateSlot& sl) {
@@ -150,7 +149,7 @@ __device__ __forceinline__ void gate_scores_wave(const float* __restrict__ zpart
     for (int j = 0; j < 8; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        v[j][i] = (lane + 64 * i < E) ? ld<COH>(zp + (ks + j) * split_stride + 64 * i) : 0.f;
+        v[j][i] = (lane + 64 * i < E) ? zp[(ks + j) * split_stride + 64 * i] : 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -159,7 +158,7 @@ __device__ __forceinline__ void gate_scores_wave(const float* __restrict__ zpart
   for (; ks < ksplit; ++ks)
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      if (lane + 64 * i < E) z[i] += ld<COH>(zp + ks * split_stride + 64 * i);
+      if (lane + 64 * i < E) z[i] += zp[ks * split_stride + 64 * i];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
