@@ -136,7 +136,7 @@ __device__ bool stalled(const int* ctl) {
 }
 
 __global__ __launch_bounds__(DEC_THREADS, 4) void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<DEC_ROWS>::SMEM];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<DEC_ROWS>::SMEM<false>];
   __shared__ int s_ok;
   const FfnArgs& f = a.f;
   const int b = blockIdx.x;

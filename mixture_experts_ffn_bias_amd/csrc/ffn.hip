@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
 // (64-element K blocks, no scales, h stored as bf16).
 template <bool UP, int ROWS, bool BF>
 __global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_tiled_kernel(FfnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<ROWS>::SMEM];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<ROWS>::template SMEM<BF>];
   Item<ROWS> it;
   if (!(UP ? up_item<ROWS, BF>(a, blockIdx.x, it) : down_item<ROWS, BF>(a, blockIdx.x, it)))
     return;  // uniform for the whole block, before any barrier

@@ -48,8 +48,8 @@ struct FfnArgs {
 //   down-projection: two consecutive 128-feature blocks of w2.
 // Per 128-deep K block, the e4m3 weight (256 x 128 B) and activation
 // (128 x 128 B) tiles and the activation scales are copied global -> LDS
-// directly (global_load_lds, no register staging) into one of three stage
-// buffers, two K blocks ahead of the multiply.  Rows are stored unpadded with
+// directly (global_load_lds, no register staging) into one of two stage
+// buffers, one K block ahead of the multiply.  Rows are stored unpadded with
 // their 16-byte chunks XOR-permuted (swz), which makes the MFMA-layout reads
 // bank-conflict free.  Wave (wr, wc) multiplies rows [64 wr, 64 wr + 64) by
 // weight rows {32 wc .. 32 wc + 31} of both groups: 4 x 4 block products per
@@ -69,7 +69,13 @@ constexpr int CPOL_SC1 = 16;                 // ... of an agent-coherent load (c
 
 // Shape of the LDS pipeline for tiles of ROWS activation rows.  A stage holds
 // one K block: the 256 weight rows, the ROWS activation rows and their scales.
-//   ROWS = 128: three stages (two K blocks in flight), one workgroup per CU.
+// NSTAGE<BF> stages: the copies of NSTAGE - 1 K blocks are in flight while
+// one is multiplied.
+//   ROWS = 128, one workgroup per CU (its registers allow no more): two
+//     stages (97 KiB) with e4m3 weights, where a third measured 3-4 % slower
+//     on every large batch; three (146 KiB) with bf16 weights, which carry
+//     twice the bytes and no decode work and measured 12 % faster with the
+//     third.
 //   ROWS = 32 (small batches, where the weights are the traffic): two stages
 //     of 36 KiB and at most 128 VGPRs, so two workgroups share a CU and one's
 //     start-up and epilogue overlap the other's weight stream.
@@ -79,8 +85,10 @@ struct Tile {
   static constexpr int B_BYTES = ROWS * BLK;
   static constexpr int S_BYTES = ROWS * 4;
   static constexpr int STAGE = TT_A_BYTES + B_BYTES + S_BYTES;
-  static constexpr int NSTAGE = ROWS == 128 ? 3 : 2;
-  static constexpr int SMEM = NSTAGE * STAGE;
+  template <bool BF>
+  static constexpr int NSTAGE = ROWS == 128 && BF ? 3 : 2;
+  template <bool BF>
+  static constexpr int SMEM = NSTAGE<BF> * STAGE;
   static constexpr int OCC = ROWS == 128 ? 1 : 2;       // workgroups per CU (8 waves each: 2 OCC waves per SIMD)
   static constexpr int APW = ROWS == 128 ? 2 : 1;       // 8-row activation pieces per copying wave
   static constexpr int AWAVES = ROWS / (8 * APW);       // waves that copy activation rows
@@ -263,7 +271,8 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS
                                                const_f32_ptr sa1, int nkb, int nrows,
                                                v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
   using G = Tile<ROWS>;
-  constexpr int AHEAD = G::NSTAGE - 1;  // K blocks whose copies are in flight during a multiply
+  constexpr int NS = G::template NSTAGE<BF>;
+  constexpr int AHEAD = NS - 1;  // K blocks whose copies are in flight during a multiply
   const int wave = threadIdx.x >> 6;
 
   const bool act = wave < G::AWAVES && 16 * ((wave * G::APW * 8) >> 4) < nrows;
@@ -286,14 +295,14 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS
   int cur = 0;  // stage buffer holding K block kb
   for (int kb = 0; kb < nkb; ++kb) {
     if (kb + AHEAD < nkb) {
-      const int nb = cur == 0 ? G::NSTAGE - 1 : cur - 1;  // (kb + AHEAD) % NSTAGE
+      const int nb = cur == 0 ? NS - 1 : cur - 1;  // (kb + AHEAD) % NS
       tile_issue<ROWS, BF, WPOL, SPOL>(src, smem + nb * G::STAGE, kb + AHEAD, wave, act);
     }
     // a wave whose 64 rows hold no tile row (MV = 0) only helps with the copies
     kblock_multiply<ROWS, BF, MV>(smem + cur * G::STAGE, sa0, sa1, kb, acc);
     if (kb + 1 < nkb) wait_vmcnt_upto(per_stage * (min(kb + AHEAD, nkb - 1) - kb - 1));
     pipeline_barrier();
-    cur = cur == G::NSTAGE - 1 ? 0 : cur + 1;
+    cur = cur == NS - 1 ? 0 : cur + 1;
   }
 }
 
@@ -579,7 +588,7 @@ __device__ __forceinline__ void zero_acc(v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
       for (int m = 0; m < Tile<ROWS>::MVMAX; ++m) acc[gi][jt][m] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
-// All K blocks and the epilogue of one item; smem: Tile<ROWS>::SMEM bytes of
+// All K blocks and the epilogue of one item; smem: Tile<ROWS>::SMEM<BF> bytes of
 // LDS.  Called by every thread of a 512-thread workgroup.  COH (for the
 // single-launch layer kernel, where other workgroups of the same launch
 // produce the activations and consume the outputs): the outputs are written
