@@ -15,7 +15,10 @@ namespace moe {
 // 256 ints of LDS.  Routed experts [e_lo, e_hi)
 // are numbered from e_lo; with has_shared the shared expert (number
 // e_hi - e_lo, rows [T*K, T*K + T)) is planned first.  once = 1 marks the
-// only tile of its expert.  At most cap routed tiles are written.  COH: the
+// only tile of its expert.  An expert with more rows than one tile holds
+// gets ceil(rows / NT) tiles of equal size (rounded up to 16 rows, the MFMA
+// sub-tile): every tile then streams the same weights, and even sizes give
+// each item the same share of multiply work to overlap with that stream.  At most cap routed tiles are written.  COH: the
 // list is written with agent-coherent stores (common.h, ld / st).
 template <bool COH = false>
 __device__ __forceinline__ void plan_tiles_block(int lo, int cnt, int T, int K, int NT, int has_shared, int cap,
@@ -37,8 +40,9 @@ __device__ __forceinline__ void plan_tiles_block(int lo, int cnt, int T, int K, 
     __syncthreads();
   }
   const int base = act ? s[e] - n : 0;
+  const int rt = n > 1 ? min(NT, ((cnt + n - 1) / n + 15) / 16 * 16) : NT;
   for (int j = 0; j < n && base + j < cap; ++j)
-    st16<COH>(tiles + nsh + base + j, make_uint4(e - e_lo, lo + j * NT, min(NT, cnt - j * NT), n == 1 ? 1 : 0));
+    st16<COH>(tiles + nsh + base + j, make_uint4(e - e_lo, lo + j * rt, min(rt, cnt - j * rt), n == 1 ? 1 : 0));
   if (threadIdx.x == 0) st<COH>(n_tiles, (int32_t)(nsh + min(s[255], cap)));
 }
 

@@ -338,14 +338,21 @@ def full_params():
 
 
 def _sample_tokens(r, T, K, n_random, seed, tile=128):
-    """Random tokens plus tokens that sit at 128-row tile edges of the busiest experts."""
+    """Random tokens plus tokens that sit at the FFN tile edges of the busiest experts.
+
+    An expert with n > tile rows is cut into ceil(n / tile) tiles of equal size,
+    rounded up to 16 rows; the edges sampled here follow that rule."""
     rng = np.random.default_rng(seed)
     pick = set(rng.choice(T, min(n_random, T), replace=False).tolist())
     perm = oracle.permute(r["idx"], r["idx"].max() + 1)
     counts = perm["counts"]
     for e in np.argsort(-counts)[:2]:
         lo, hi = perm["offsets"][e], perm["offsets"][e + 1]
-        for pos in (lo, hi - 1, lo + tile - 1, lo + tile):
+        n = hi - lo
+        nt = -(-n // tile)
+        rt = min(tile, -(-(-(-n // nt)) // 16) * 16) if nt > 1 else tile
+        edges = [lo, hi - 1] + [lo + j * rt + d for j in range(1, nt) for d in (-1, 0)]
+        for pos in edges:
             if lo <= pos < hi:
                 pick.add(int(perm["row_token"][pos]))
     return np.array(sorted(pick))
