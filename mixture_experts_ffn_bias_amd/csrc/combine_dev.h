@@ -22,6 +22,13 @@ namespace moe {
 
 namespace {
 
+// 16 bytes of an expert output row, read with the non-temporal hint: each
+// row is read once, by one workgroup, in whole 128-byte lines per wave.
+__device__ __forceinline__ uint4 ld_nt16(const uint16_t* p) {
+  const v4i v = __builtin_nontemporal_load((const v4i*)p);
+  return make_uint4((uint32_t)v[0], (uint32_t)v[1], (uint32_t)v[2], (uint32_t)v[3]);
+}
+
 // PARTIAL: y (fp32) = the sum over choices with expert in [e_lo, e_hi), plus
 // the shared row when has_shared; otherwise delta (bf16) = bf16(full sum).
 // Token t, share `part` of `nparts` of the row (8-element chunks); called by
@@ -83,18 +90,27 @@ __device__ __forceinline__ void combine_token(const int32_t* __restrict__ idx, c
     float y[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) y[i] = 0.f;
-    for (int k = 0; k < n; ++k) {
-      const uint4 v = *(const uint4*)(rows + (size_t)s_row[k] * d + c * 8);
-      const float wk = s_w[k];
-      const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    // up to 8 rows loaded together (all in flight), then added in order
+    for (int k0 = 0; k0 < n; k0 += 8) {
+      uint4 v[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        y[2 * i] = fmaf(wk, bf16_to_f32(u[i] & 0xFFFFu), y[2 * i]);
-        y[2 * i + 1] = fmaf(wk, bf16_to_f32(u[i] >> 16), y[2 * i + 1]);
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < n) v[j] = ld_nt16(rows + (size_t)s_row[k0 + j] * d + c * 8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if (k0 + j < n) {
+          const float wk = s_w[k0 + j];
+          const uint32_t u[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            y[2 * i] = fmaf(wk, bf16_to_f32(u[i] & 0xFFFFu), y[2 * i]);
+            y[2 * i + 1] = fmaf(wk, bf16_to_f32(u[i] >> 16), y[2 * i + 1]);
+          }
+        }
       }
     }
     if (has_shared) {
-      const uint4 v = *(const uint4*)(rows + (size_t)(TK + t) * d + c * 8);
+      const uint4 v = ld_nt16(rows + (size_t)(TK + t) * d + c * 8);
       const uint32_t u[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
       for (int i = 0; i < 4; ++i) {

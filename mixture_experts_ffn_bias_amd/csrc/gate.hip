@@ -170,7 +170,8 @@ int gate_ksplit(int64_t T, int d, int E) {
   const int ntw = gate_tiles_per_wave(T);
   int64_t base = ((T + 63) / 64) * ((E + 16 * ntw - 1) / (16 * ntw));
   if (base < 1) base = 1;
-  int64_t ks = (512 + base - 1) / base;
+  const int64_t target = ntw == 4 ? 2048 : 512;
+  int64_t ks = (target + base - 1) / base;
   const int ksteps = d / 32;
   if (ks > ksteps) ks = ksteps;
   if (ks > GATE_KSPLIT_MAX) ks = GATE_KSPLIT_MAX;
