@@ -189,6 +189,55 @@ def test_grouped_ffn_forced_routing_tiny(tiny_params, T):
     assert_rows_close(got, ref, f"grouped_ffn tiny T={T}")
 
 
+def _idx_with_counts(counts, T, K):
+    """A [T, K] routing in which expert e is chosen by exactly counts[e] tokens, K distinct experts per token.
+
+    The expert ids, each repeated counts[e] times in ascending order, fill the matrix column by column; an
+    expert's copies are at most T consecutive slots, so they land on distinct tokens."""
+    ids = np.repeat(np.arange(len(counts)), counts)
+    assert ids.size == T * K and max(counts) <= T
+    return ids.reshape(K, T).T.copy()
+
+
+@pytest.mark.parametrize("T,counts", [
+    # 32-row tiles (T <= 128): ragged tails and experts cut into two or three equal tiles
+    (100, [0, 1, 15, 16, 17, 31, 32, 33, 48, 49, 63, 65, 30, 0, 0, 0]),
+    # 128-row tiles: 127 / 129 / 144 / 160 / 193 / 200 rows are cut into two equal 16-row-aligned tiles
+    (300, [0, 1, 15, 16, 17, 31, 33, 63, 127, 129, 144, 160, 193, 200, 71, 0]),
+])
+def test_grouped_ffn_tile_edges(tiny_params, T, counts):
+    _say(f"moe_grouped_ffn tile edges T={T}")
+    dims = synth.TINY
+    K, E, d = dims.topk, dims.n_experts, dims.d_model
+    idx = _idx_with_counts(np.array(counts), T, K)
+    x = synth.make_x(dims, T, DEV, seed=90 + T)
+    pn = _np_params(tiny_params)
+    xv = f64(x)
+    perm = oracle.permute(idx, E)
+    assert np.array_equal(perm["counts"], counts)
+    xq, xs = oracle.quant_act(xv)
+    rows_tok = np.concatenate([perm["row_token"], np.arange(T)]).astype(np.int32)
+    cd = cdims(dims)
+    out = torch.zeros((T * K + T, d), dtype=torch.bfloat16, device=DEV)
+    routed = moe.experts_struct(*(tiny_params[k] for k in ("w1", "w3", "w2", "s1", "s3", "s2")))
+    shared = moe.experts_struct(*(tiny_params["sh_" + k] for k in ("w1", "w3", "w2", "s1", "s3", "s2")))
+    moe.moe_grouped_ffn(cd, T, routed, shared, torch.from_numpy(perm["offsets"]).int().to(DEV),
+                        torch.from_numpy(rows_tok).to(DEV), torch.from_numpy(xq).to(DEV),
+                        torch.from_numpy(xs).to(DEV), out, moe.workspace(cd, T))
+    torch.cuda.synchronize()
+    got = f64(out)
+    ref = np.zeros_like(got)
+    off = perm["offsets"]
+    for e in range(E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size:
+            ref[rows] = oracle.expert_ffn(xv[perm["row_token"][rows]], pn["w1"][e], pn["s1"][e], pn["w3"][e],
+                                          pn["s3"][e], pn["w2"][e], pn["s2"][e])
+    ref[T * K:] = oracle.expert_ffn(xv, pn["sh_w1"][0], pn["sh_s1"][0], pn["sh_w3"][0], pn["sh_s3"][0],
+                                    pn["sh_w2"][0], pn["sh_s2"][0])
+    assert_rows_close(got, ref, f"grouped_ffn tile edges T={T}")
+
+
 def test_grouped_ffn_without_shared_leaves_shared_rows(tiny_params):
     _say("moe_grouped_ffn shared=NULL")
     dims = synth.TINY
