@@ -595,6 +595,38 @@ def test_grouped_ffn_bf16_forced_routing_tiny(tiny_params_bf16, T):
     assert_rows_close(got, ref, f"grouped_ffn_bf16 tiny T={T}")
 
 
+@pytest.mark.parametrize("T,counts", [
+    (100, [0, 1, 15, 16, 17, 31, 32, 33, 48, 49, 63, 65, 30, 0, 0, 0]),
+    (300, [0, 1, 15, 16, 17, 31, 33, 63, 127, 129, 144, 160, 193, 200, 71, 0]),
+])
+def test_grouped_ffn_bf16_tile_edges(tiny_params_bf16, T, counts):
+    _say(f"moe_grouped_ffn_bf16 tile edges T={T}")
+    dims, p = synth.TINY, tiny_params_bf16
+    K, E, d = dims.topk, dims.n_experts, dims.d_model
+    idx = _idx_with_counts(np.array(counts), T, K)
+    x = synth.make_x(dims, T, DEV, seed=95 + T)
+    pn = _np_params(p)
+    xv = f64(x)
+    perm = oracle.permute(idx, E)
+    rows_tok = np.concatenate([perm["row_token"], np.arange(T)]).astype(np.int32)
+    cd = cdims(dims)
+    out = torch.zeros((T * K + T, d), dtype=torch.bfloat16, device=DEV)
+    routed = moe.experts_struct_bf16(p["w1"], p["w3"], p["w2"])
+    shared = moe.experts_struct_bf16(p["sh_w1"], p["sh_w3"], p["sh_w2"])
+    moe.moe_grouped_ffn_bf16(cd, T, routed, shared, torch.from_numpy(perm["offsets"]).int().to(DEV),
+                             torch.from_numpy(rows_tok).to(DEV), x, out, moe.workspace(cd, T))
+    torch.cuda.synchronize()
+    got = f64(out)
+    ref = np.zeros_like(got)
+    off = perm["offsets"]
+    for e in range(E):
+        rows = np.arange(off[e], off[e + 1])
+        if rows.size:
+            ref[rows] = oracle.expert_ffn_bf16(xv[perm["row_token"][rows]], *_bf16_expert(pn, "", e))
+    ref[T * K:] = oracle.expert_ffn_bf16(xv, *_bf16_expert(pn, "sh_", 0))
+    assert_rows_close(got, ref, f"grouped_ffn_bf16 tile edges T={T}")
+
+
 @pytest.mark.parametrize("T", [1, 37, 64, 1000])
 def test_forward_bf16_tiny(tiny_params_bf16, T):
     _say(f"moe_forward_bf16 tiny T={T}")
