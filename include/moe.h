@@ -107,7 +107,8 @@ typedef struct {
  * needs for `tokens` tokens.  Returns 0 for invalid dims. */
 size_t moe_workspace_size(const moe_dims* dims, int64_t tokens);
 
-/* Router: ``weights, indices = self.gate(x)`` ("MoE update", moe-forward excerpt).
+/* Router: the gate call of the moe-forward excerpt on "MoE update", which
+ * returns each token's routing weights and expert indices.
  *   x       bf16 [T][d]   (16-byte aligned)
  *   gate_w  fp32 [E][d]   (16-byte aligned), gate_b fp32 [E]
  *   idx     int32 [T][K]  out: selected experts, descending biased score
@@ -120,9 +121,10 @@ int moe_gate(const moe_dims* dims, int64_t tokens, const uint16_t* x, const floa
              const float* gate_b, int32_t* idx, float* w, void* workspace, size_t workspace_bytes,
              void* stream);
 
-/* Token counting and expert-contiguous order (``bincount`` and
- * ``torch.where(indices == i)``, "MoE update", moe-forward excerpt), plus the
- * FP8 activation quantisation the expert Linear layers consume.
+/* Token counting and expert-contiguous order (the moe-forward excerpt on
+ * "MoE update" counts the tokens of each expert and gathers them expert by
+ * expert), plus the FP8 activation quantisation the expert Linear layers
+ * consume.
  *   idx        int32 [T][K]      routing from moe_gate
  *   x          bf16  [T][d]      (16-byte aligned)
  *   counts     int32 [E]         out: rows per expert
@@ -140,8 +142,9 @@ int moe_permute(const moe_dims* dims, int64_t tokens, const int32_t* idx, const 
                 int32_t* counts, int32_t* offsets, int32_t* row_token, int32_t* pair_row,
                 uint8_t* xq, float* xs, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Grouped expert FFN over the permuted rows ("Gate projection": expert
- * excerpt ``w2((silu(w1(x).float()) * w3(x).float()).type_as(x))``):
+/* Grouped expert FFN over the permuted rows ("Gate projection", expert
+ * excerpt: SwiGLU of the two input projections taken in fp32, the product
+ * cast back to the input dtype, then the output projection):
  * for every row r of expert e (and every shared-expert row),
  *   g = bf16(Q(x) . W1_e^T), u = bf16(Q(x) . W3_e^T), h = bf16(silu(g) * u),
  *   out[r] = bf16(Q(h) . W2_e^T)
@@ -170,9 +173,10 @@ int moe_grouped_ffn_bf16(const moe_dims* dims, int64_t tokens, const moe_experts
                          const uint16_t* x, uint16_t* out, void* workspace, size_t workspace_bytes,
                          void* stream);
 
-/* Router-weighted combine plus shared output ("MoE update": ``y[idx] +=
- * expert(x[idx]) * weights[idx, top]`` in ascending expert order, then
- * ``y += shared_experts(x)``, then ``y.type_as(x)``):
+/* Router-weighted combine plus shared output ("MoE update", moe-forward
+ * excerpt: each expert's rows, scaled by their routing weights, are added to
+ * an fp32 accumulator expert by expert in ascending order, then the shared
+ * expert's output, then the sum is cast back to x's dtype):
  *   delta[t] = bf16( sum over k in ascending idx[t][k] of w[t][k] * rows[pair_row[t][k]]
  *                    + rows[T*K + t] )     accumulated in fp32.
  *   rows    bf16 [T*K + T][d] from moe_grouped_ffn (16-byte aligned)
@@ -215,8 +219,8 @@ int moe_forward_bf16_timed(const moe_dims* dims, const moe_weights_bf16* weights
                            void* const* stage_events);
 
 /* One rank's share of an expert-parallel layer ("MoE update", moe-forward
- * excerpt: a rank runs only experts [experts_start_idx, experts_end_idx) and
- * the ranks' y are summed by an all-reduce before the cast to the input dtype).
+ * excerpt: a rank runs only its contiguous slice of the experts, and the
+ * ranks' y are summed by an all-reduce before the cast to the input dtype).
  *   expert_begin, expert_end  the rank's routed experts, 0 <= begin < end <= E
  *   weights->routed           holds exactly those end - begin experts, expert_begin first
  *   with_shared               1: add the shared expert (one rank of the group does);

@@ -1,8 +1,8 @@
 // Router-weighted combine and shared-expert add ("DeepSeek-V3.2-Exp · MoE
-// update", moe-forward excerpt: ``y[idx] += expert(x[idx]) * weights[idx, top]``
-// over experts in ascending id into an fp32 accumulator, ``y +=
-// shared_experts(x)``, then the cast back to the input dtype;
-// "DeepSeek-V3.2-Exp · Add shared output", formula).
+// update", moe-forward excerpt: each expert's output rows, times their
+// routing weights, accumulate into fp32 expert by expert in ascending id, the
+// shared expert's output is added, and the sum is cast back to the input
+// dtype; "DeepSeek-V3.2-Exp · Add shared output", formula).
 //
 // One workgroup per token and share of the row (small batches split each row
 // over several workgroups to occupy the chip); the token's K rows are visited
@@ -10,8 +10,8 @@
 // loop and the result is deterministic (no atomics).
 //
 // The partial form serves one rank of an expert-parallel layer: it sums only
-// the experts [e_lo, e_hi) a rank holds (the pages' experts_start_idx ..
-// experts_end_idx slice) and leaves y in fp32 for the cross-rank sum.
+// the experts [e_lo, e_hi) a rank holds (its slice of the experts in the
+// pages' expert-parallel loop) and leaves y in fp32 for the cross-rank sum.
 //
 // Device function shared by the combine kernels and the single-launch layer
 // kernel.

@@ -1,7 +1,8 @@
 // Grouped SwiGLU expert FFN with FP8 (e4m3) weights and activations
-// ("DeepSeek-V3.2-Exp · Gate projection": expert excerpt
-// ``w2((silu(w1(x).float()) * w3(x).float()).type_as(x))`` and Linear excerpt:
-// FP8 weights [out, in] with one fp32 scale per 128x128 block).
+// ("DeepSeek-V3.2-Exp · Gate projection": the expert excerpt, SwiGLU of the
+// w1 and w3 projections taken in fp32, cast back to the input dtype, then w2;
+// the Linear excerpt: FP8 weights [out, in] with one fp32 scale per 128x128
+// block).
 //
 // Work unit ("tile"): up to 128 consecutive permuted rows of one expert.
 // Up-projection workgroups own (tile, 128-column block of h) and hold the w1

@@ -1,5 +1,5 @@
 // Token counting and expert-contiguous order ("DeepSeek-V3.2-Exp · MoE update",
-// moe-forward excerpt: bincount of the selected experts, then for each expert
+// moe-forward excerpt: a count of the selected experts, then for each expert
 // the tokens that chose it in ascending token order), and the FP8 quantisation
 // of x that the expert Linear layers consume.
 //

@@ -1,5 +1,5 @@
 // Token counting, expert-contiguous order and activation quantisation
-// ("DeepSeek-V3.2-Exp · MoE update", moe-forward excerpt: bincount of the
+// ("DeepSeek-V3.2-Exp · MoE update", moe-forward excerpt: a count of the
 // selected experts, then for each expert the tokens that chose it in
 // ascending token order; "DeepSeek-V3.2-Exp · Gate projection", the FP8
 // Linear's activation quantisation), as device functions shared by the

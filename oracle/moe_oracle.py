@@ -7,40 +7,43 @@ shares no code, table or helper with the HIP library.
 What it computes, and where each step comes from (page titles as printed):
 
 * "DeepSeek-V3.2-Exp · MoE update", moe-forward excerpt: tokens are
-  flattened to [N, d]; ``weights, indices = gate(x)``; an fp32 accumulator y;
-  ``bincount`` of the selected experts; a loop over experts in ascending id
+  flattened to [N, d]; the gate returns routing weights and expert indices;
+  an fp32 accumulator y; a count of the tokens per selected expert; a loop
+  over experts in ascending id
   that gathers the tokens routed to the expert in ascending token order,
   runs the expert and adds its output times the router weight; then the
   shared expert's output for every token; finally y is cast back to the
   input dtype (the page's output expression).
 * "DeepSeek-V3.2-Exp · Add shared output", formula: the update is the routed
   sum plus the shared-expert output.
-* "DeepSeek-V3.2-Exp · Gate projection", expert excerpt: an expert is
-  ``w2((silu(w1(x).float()) * w3(x).float()).type_as(x))``; Linear excerpt:
-  weights are [out, in], FP8 weights carry one float32 scale per 128x128
-  block (``block_size = 128``), wider (bf16) weights carry none, no bias.
+* "DeepSeek-V3.2-Exp · Gate projection", expert excerpt: an expert applies
+  w1 and w3, takes SiLU of the first times the second in float32, casts the
+  product back to the input dtype and applies w2; Linear excerpt: weights
+  are [out, in], FP8 weights carry one float32 scale per 128x128 block, wider
+  (bf16) weights carry none, no bias.
 * "DeepSeek-V3.2-Exp · MoE update", rmsnorm excerpt: with a residual, the
   residual is added in float32, the sum (cast back) becomes the new residual,
-  and the normalised sum is ``weight * x * rsqrt(mean(x^2) + eps)``, eps 1e-6.
+  and the output is the gain times the sum divided by the root of its mean
+  square plus eps, eps 1e-6.
 * "MoE transformer block", parameter accounting table: the MoE of one block
   has 11,320,164,608 parameters; with 256 routed + 1 shared expert of shape
   7168->2048->7168 the remainder is exactly a 256x7168 router weight plus a
   256-element router bias.
 
-The pages show only the call ``gate(x)``.  The router used here is the plain
+The pages show only the gate's call site.  The router used here is the plain
 reading of the layer's description: sigmoid scores of x.Wg^T, a per-expert
 bias added for selection only, groups scored by the sum of their two largest
-biased scores, the top ``topk_groups`` groups kept (the others excluded), the
-top ``topk`` biased scores among kept experts selected, and weights equal to
+biased scores, the top topk_groups groups kept (the others excluded), the
+top topk biased scores among kept experts selected, and weights equal to
 the unbiased scores of the selected experts normalised to sum 1 and multiplied
-by ``route_scale``.  Ties go to the lower group / expert index.
+by route_scale.  Ties go to the lower group / expert index.
 
 The pages also omit how an FP8 Linear multiplies (the Linear excerpt skips
 that part of the file).  The reading used here: the bf16 activation row is
 quantised per 128-element block to e4m3 with scale = block amax / 448 (the
 same rule the weights use), the block products are summed exactly, and the
 Linear output is rounded to bfloat16 (it returns the activation dtype, which
-is why the expert calls ``.float()`` on it).
+is why the expert converts it to float32 before SiLU).
 
 Every floating-point step is evaluated in float64 (exact for all e4m3 x e4m3
 block sums); the roundings the pages place (bf16 Linear outputs, bf16 h,
@@ -54,7 +57,7 @@ from typing import Dict, Optional, Sequence
 import numpy as np
 import torch
 
-BLOCK = 128          # "Gate projection", Linear excerpt: block_size = 128
+BLOCK = 128          # "Gate projection", Linear excerpt: the FP8 scale block edge
 E4M3_MAX = 448.0     # largest finite e4m3fn value (OCP 8-bit floating point, E4M3)
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
 RMS_EPS = 1e-6       # "MoE update", rmsnorm excerpt: eps default
@@ -187,7 +190,8 @@ def dequant_act(codes, scale) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
-# Router ("MoE update", moe-forward excerpt: weights, indices = self.gate(x))
+# Router ("MoE update", moe-forward excerpt: the gate call, which returns the
+# routing weights and the expert indices)
 # --------------------------------------------------------------------------
 
 def gate(x, gate_w, gate_b, dims) -> Dict[str, np.ndarray]:
@@ -238,7 +242,7 @@ def weights_for(s_rows, idx, route_scale) -> np.ndarray:
 
 # --------------------------------------------------------------------------
 # Token counting and expert-contiguous order ("MoE update", moe-forward excerpt:
-# bincount, then torch.where(indices == i) per expert)
+# a count per expert, then each expert's tokens gathered in ascending order)
 # --------------------------------------------------------------------------
 
 def permute(idx, n_experts: int) -> Dict[str, np.ndarray]:

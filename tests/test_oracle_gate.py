@@ -1,7 +1,7 @@
 """Pins of the oracle's router.
 
-The pages show only ``weights, indices = self.gate(x)`` ("MoE update",
-moe-forward excerpt); the router's steps are the plain reading written in the
+The pages show only the gate's call site ("MoE update", moe-forward
+excerpt: it returns routing weights and expert indices); the router's steps are the plain reading written in the
 oracle's header.  Pins: exhaustive subset search (a different algorithm for
 the same selection), a special case that reduces to a plain top-k of the
 logits, hand-worked examples whose answers follow from the definition, and the
