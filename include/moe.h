@@ -281,9 +281,9 @@ int moe_add_rmsnorm(int32_t d, int64_t tokens, const uint16_t* x, uint16_t* resi
 size_t moe_mlp_workspace_size(int32_t d_model, int32_t inter, int64_t tokens);
 
 /* Dense MLP of the blocks that precede the MoE blocks ("DeepSeek-V3.2-Exp ·
- * MoE update", block excerpt: the first n_dense_layers blocks build
- * MLP(dim, inter_dim) where the others build the MoE).  The pages print
- * neither the MLP's body nor inter_dim; it is taken to be the SwiGLU of one
+ * MoE update", block excerpt: the first few blocks build a dense MLP of the
+ * model width where the others build the MoE).  The pages print neither the
+ * MLP's body nor its hidden width; it is taken to be the SwiGLU of one
  * expert in the same FP8 form ("Gate projection", expert and Linear excerpts):
  *   out[t] = bf16(Q(h) . W2^T),  h = bf16(silu(bf16(Q(x[t]) . W1^T)) * bf16(Q(x[t]) . W3^T))
  * with Q the per-128-block e4m3 activation quantiser of moe_grouped_ffn.
