@@ -273,7 +273,8 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS
   using G = Tile<ROWS>;
   constexpr int NS = G::template NSTAGE<BF>;
   constexpr int AHEAD = NS - 1;  // K blocks whose copies are in flight during a multiply
-  const int wave = threadIdx.x >> 6;
+  // scalar wave index: the LDS addresses of the copies are computed with scalar instructions
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   const bool act = wave < G::AWAVES && 16 * ((wave * G::APW * 8) >> 4) < nrows;
   const int per_stage = tile_copies<ROWS, BF>(wave, act);
@@ -292,17 +293,31 @@ __device__ __forceinline__ void tiled_mainloop(uint8_t* smem, const TileSrc<ROWS
   // block kb - 1 used (every wave left it at the last barrier), multiplies
   // block kb, then waits for its own copies of block kb + 1 (all but those of
   // the blocks issued after it); the barrier publishes that stage.
-  int cur = 0;  // stage buffer holding K block kb
-  for (int kb = 0; kb < nkb; ++kb) {
-    if (kb + AHEAD < nkb) {
-      const int nb = cur == 0 ? NS - 1 : cur - 1;  // (kb + AHEAD) % NS
-      tile_issue<ROWS, BF, WPOL, SPOL>(src, smem + nb * G::STAGE, kb + AHEAD, wave, act);
-    }
+  auto step = [&](int cur, int kb) {  // cur = kb % NS
+    const int nb = cur == 0 ? NS - 1 : cur - 1;  // (kb + AHEAD) % NS
+    if (kb + AHEAD < nkb) tile_issue<ROWS, BF, WPOL, SPOL>(src, smem + nb * G::STAGE, kb + AHEAD, wave, act);
     // a wave whose 64 rows hold no tile row (MV = 0) only helps with the copies
     kblock_multiply<ROWS, BF, MV>(smem + cur * G::STAGE, sa0, sa1, kb, acc);
     if (kb + 1 < nkb) wait_vmcnt_upto(per_stage * (min(kb + AHEAD, nkb - 1) - kb - 1));
     pipeline_barrier();
-    cur = cur == NS - 1 ? 0 : cur + 1;
+  };
+  if constexpr (ROWS == 128) {
+    // unrolled over the NS stages: each stage's LDS offsets are constants, so
+    // the addresses need no per-block arithmetic (prefill -2 %; the 32-row
+    // kernels would spill)
+    for (int kb = 0; kb < nkb; kb += NS) {
+      step(0, kb);
+      if (kb + 1 < nkb) step(1, kb + 1);
+      if constexpr (NS == 3) {
+        if (kb + 2 < nkb) step(2, kb + 2);
+      }
+    }
+  } else {
+    int cur = 0;
+    for (int kb = 0; kb < nkb; ++kb) {
+      step(cur, kb);
+      cur = cur == NS - 1 ? 0 : cur + 1;
+    }
   }
 }
 
