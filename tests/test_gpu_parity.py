@@ -448,6 +448,16 @@ def test_forward_full_skewed(full_params):
     _full_case(full_params, bias, 16384, seed=103, n_random=3)
 
 
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_forward_full_large_batch(full_params):
+    """The largest batch of the suite: 65,536 tokens (524,288 routed rows, ~16 tiles per
+    expert, ~4,600 tiles), so the launches' grids, tile counts and row offsets run far
+    beyond those of the named workloads."""
+    _say("moe_forward full shape T=65536 bias 0 (large batch)")
+    _full_case(full_params, torch.zeros(256, device=DEV), 65536, seed=104, n_random=3)
+
+
 # ----------------------------------------------------------------------------
 # stack of four blocks: fused residual-add RMSNorm + layer, residual in bf16
 # ----------------------------------------------------------------------------
