@@ -1,7 +1,7 @@
 """Benchmark of the DeepSeek-V3.2-Exp MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|stack4|tiny]
-                    [--weights e4m3|bf16] [--ep-share N]
+                    [--weights e4m3|bf16] [--ep-share N] [--fused] [--no-cpu-baseline]
 
 A step is one pass of the whole layer (router, permutation, grouped expert
 FFN, combine; for the stacked workload four blocks of fused residual-add
