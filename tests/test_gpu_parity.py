@@ -413,6 +413,8 @@ def _full_case(params, bias, T, seed, n_random):
     p["gate_b"] = bias
     x = synth.make_x(dims, T, DEV, seed=seed)
     delta, gi, gw = run_forward(dims, p, x)
+    again, gi2, gw2 = run_forward(dims, p, x)        # no atomics, fixed sum orders: bit-identical
+    assert torch.equal(delta, again) and np.array_equal(gi, gi2) and np.array_equal(gw, gw2)
     hv = HostView(p)
     xv = f64(x)
     r = oracle.gate(xv, hv["gate_w"], hv["gate_b"], dims)
