@@ -272,6 +272,10 @@ class MoELayer:
     w2 uint8 [E, d, I], s1/s3 fp32 [E, I/128, d/128], s2 fp32 [E, d/128, I/128],
     and the same with an ``sh_`` prefix for the shared expert (leading dim 1).
     With bf16 w1/w3/w2 (and no scales) the layer runs moe_forward_bf16.
+
+    The layer keeps one workspace (grown on demand) that every call uses: calls
+    on different streams must be ordered by the caller (an event or a sync),
+    as must a call that grows the workspace after a call on another stream.
     """
 
     def __init__(self, dims: moe_dims, params: Dict[str, torch.Tensor]):
