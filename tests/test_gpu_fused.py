@@ -112,6 +112,31 @@ def test_fused_hot_group_multi_tile_experts(tiny_params):
     check_against_oracle(dims, p, x, delta, gi, gw, "fused hot group")
 
 
+# int32 index of the "a wait gave up" word in the workspace's control block (kernels.h: DEC_CTL_STALLED)
+CTL_STALLED = 192
+
+
+def test_fused_reports_a_stall_and_recovers(tiny_params):
+    """A stall forced from the host: with the stall word set before the call, every bounded
+    wait gives up at its first poll, each workgroup still runs to its end, and the last one
+    resets the counts.  The status call reports MOE_ERR_STALLED; the next call on the same
+    workspace is clean and gives the same bits as before."""
+    _say("moe_forward_fused: stall word set from the host")
+    dims = synth.TINY
+    layer = moe.MoELayer(cdims(dims), tiny_params)
+    x = synth.make_x(dims, 64, DEV, seed=12)
+    good, gi, gw = run_fused(layer, x)
+    ctl = layer._fused_ws[:4096].view(torch.int32)
+    ctl[CTL_STALLED] = 1
+    torch.cuda.synchronize()
+    layer.forward_fused(x)
+    assert moe.moe_forward_fused_status(layer._fused_ws) == moe.MOE_ERR_STALLED
+    c = ctl.cpu().numpy()
+    assert c[CTL_STALLED] == 0 and np.count_nonzero(c) == 1        # only the status word is left set
+    again, gi2, gw2 = run_fused(layer, x)                           # asserts status OK
+    assert torch.equal(good, again) and np.array_equal(gi, gi2) and np.array_equal(gw, gw2)
+
+
 def test_fused_rejects_more_than_64_tokens(tiny_params):
     layer = moe.MoELayer(cdims(synth.TINY), tiny_params)
     with pytest.raises(moe.MoeError):
