@@ -1,7 +1,7 @@
 """Benchmark of the DeepSeek-V3.2-Exp MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|stack4|tiny]
-                    [--weights e4m3|bf16] [--ep-share N] [--fused] [--no-cpu-baseline]
+                    [--weights e4m3|bf16] [--ep-share N] [--fused] [--mlp INTER] [--no-cpu-baseline]
 
 A step is one pass of the whole layer (router, permutation, grouped expert
 FFN, combine; for the stacked workload four blocks of fused residual-add
@@ -222,6 +222,9 @@ def main():
     ap.add_argument("--fused", action="store_true",
                     help="time the single-launch forward (moe_forward_fused: one kernel for the whole layer, "
                          "at most 64 tokens, e4m3 weights) instead of the per-step kernels")
+    ap.add_argument("--mlp", type=int, default=0, metavar="INTER",
+                    help="time the dense SwiGLU MLP of the blocks before the MoE blocks instead (moe_mlp, FP8 "
+                         "weights d_model -> INTER -> d_model, e.g. 18432) over the workload's tokens")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -254,6 +257,8 @@ def main():
         return bench_share(args, moe, synth, torch, np, dev)
     if args.fused:
         return bench_fused(args, moe, synth, torch, np, dev)
+    if args.mlp:
+        return bench_mlp(args, moe, synth, torch, np, dev)
     wl = synth.WORKLOADS[args.workload]
     dims = wl.dims
     bf16 = args.weights == "bf16"
@@ -503,6 +508,59 @@ def bench_fused(args, moe, synth, torch, np, dev):
     print(json.dumps(out), flush=True)
     if status != 0:
         sys.exit("moe_forward_fused: a wait gave up during the timed launches")
+
+
+def bench_mlp(args, moe, synth, torch, np, dev):
+    """The dense MLP (moe_mlp) over the workload's tokens, timed launch by launch."""
+    wl = synth.WORKLOADS[args.workload]
+    d, inter = wl.dims.d_model, args.mlp
+    if args.weights != "e4m3":
+        sys.exit("--mlp takes e4m3 weights")
+    T = wl.tokens
+    x = synth.make_x(wl.dims, T, dev, wl.seed)
+    p = synth.mlp_weights(d, inter, dev, wl.seed)
+    mlp = moe.experts_struct(*(p[k] for k in ("w1", "w3", "w2", "s1", "s3", "s2")))
+    ws = moe.mlp_workspace(d, inter, T, device=dev)
+    out = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        moe.moe_mlp(d, inter, T, mlp, x, out, ws, stream)
+    hev = HipEvents()
+    K = args.steps
+    ev = hev.create(2 * K)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        hev.record(ev[2 * k], stream.cuda_stream)
+        moe.moe_mlp(d, inter, T, mlp, x, out, ws, stream)
+        hev.record(ev[2 * k + 1], stream.cuda_stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = sum(hev.ms(ev[2 * k], ev[2 * k + 1]) for k in range(K)) / K
+    hev.close()
+    wbytes = 3 * d * inter + 3 * (d // 128) * (inter // 128) * 4
+    alg_bytes = wbytes + 2 * T * d * 2                      # weights once, x in, out
+    alg_flops = 6 * T * d * inter
+    if alg_flops / alg_bytes > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
+        ach = alg_flops / (launch_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4)}
+    else:
+        ach = alg_bytes / (launch_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof.update({"kernel": "dense MLP (quantisation + up- and down-projection)", "traffic": None,
+                 "launch_ms": round(launch_ms, 4), "alg_bytes": int(alg_bytes), "alg_flops": int(alg_flops)})
+    res = {
+        "metric": "dense MLP tokens/s (d7168, FP8 SwiGLU) + % of bf16 MFMA / HBM roofline",
+        "value": round(T * K / wall, 2), "unit": "tokens/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "path": "dense MLP (moe_mlp)", "d_model": d,
+                   "inter": inter, "weights": "e4m3 + fp32 128x128 block scales"},
+        "roofline": roof, "cpu_baseline": None,
+    }
+    print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

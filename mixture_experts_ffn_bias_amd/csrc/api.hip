@@ -3,6 +3,8 @@
 // here allocates device memory or synchronises the host.
 #include <math.h>
 
+#include <algorithm>
+
 #include "../../include/moe.h"
 #include "common.h"
 #include "kernels.h"
@@ -96,7 +98,8 @@ FusedLayout fused_layout(const moe_dims& dm, int64_t T) {
 
 // Dense MLP: xq, xs, the tile list and h.
 struct MlpLayout {
-  size_t xq, xs, tiles, n_tiles, hq, hs, total;
+  size_t xq, xs, tiles, n_tiles, hq, hs, part, total;
+  int up_ks, up_kper, dn_ks, dn_kper;  // split K (part: the larger set of fp32 partial planes)
 };
 
 MlpLayout mlp_layout(int d, int I, int64_t T) {
@@ -114,6 +117,10 @@ MlpLayout mlp_layout(int d, int I, int64_t T) {
   L.n_tiles = take(4);
   L.hq = take(t * I);
   L.hs = take(t * (I / BLK) * 4);
+  ffn_dense_ksplit(T, d, I, &L.up_ks, &L.up_kper, &L.dn_ks, &L.dn_kper);
+  const size_t up_part = L.up_ks > 1 ? (size_t)L.up_ks * t * 2 * I * 4 : 0;
+  const size_t dn_part = L.dn_ks > 1 ? (size_t)L.dn_ks * t * d * 4 : 0;
+  L.part = take(std::max(up_part, dn_part));
   L.total = off;
   return L;
 }
@@ -538,9 +545,11 @@ int moe_mlp(int32_t d_model, int32_t inter, int64_t tokens, const moe_experts* m
   MOE_TRY(hip_status(launch_quant(x, tokens, d_model, xq, xs, s)));
   // one dense expert: no routed experts, rows are tokens
   const ExpertPtrs p = ptrs(*mlp);
+  const FfnSplit split{at<float>(workspace, L.part), L.up_ks, L.up_kper, L.dn_ks, L.dn_kper};
   return hip_status(launch_ffn(p, &p, (int)tokens, d_model, inter, 0, 0, nullptr, nullptr, xq, xs,
                                at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
-                               at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), out, s));
+                               at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), out, s, nullptr, false, 0,
+                               -1, false, &split));
 }
 
 const char* moe_status_string(int status) {

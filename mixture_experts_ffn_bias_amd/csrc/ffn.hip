@@ -15,6 +15,8 @@
 // acc += P * (s_weight[block] * s_act[row, block]).
 // Weights are the A operand (16 output features), activations the B operand
 // (16 rows); lane l ends with features 4*(l/16)+j of row l%16.
+#include <algorithm>
+
 #include "ffn_tile.h"
 #include "plan.h"
 
@@ -40,29 +42,108 @@ __global__ __launch_bounds__(256) void plan_tiles_kernel(const int32_t* __restri
   plan_tiles_block(lo, cnt, T, K, NT, has_shared, cap, e_lo, e_hi, s, tiles, n_tiles);
 }
 
-// One item per workgroup.  UP: grid = max_tiles * (I/128); down: grid =
-// max_tiles * ceil(d/256).  Block = 512.  BF: bf16 weights and activations
-// (64-element K blocks, no scales, h stored as bf16).
-template <bool UP, int ROWS, bool BF>
+// One item per workgroup.  UP: grid = max_tiles * items_per_tile(I/128, up_ks);
+// down: grid = max_tiles * items_per_tile(ceil(d/256), dn_ks).  Block = 512.
+// BF: bf16 weights and activations (64-element K blocks, no scales, h stored
+// as bf16).  SPLIT: the instance for split K (kept apart so that the unsplit
+// kernels carry none of its code).
+template <bool UP, int ROWS, bool BF, bool SPLIT>
 __global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_tiled_kernel(FfnArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<ROWS>::template SMEM<BF>];
   Item<ROWS> it;
-  if (!(UP ? up_item<ROWS, BF>(a, blockIdx.x, it) : down_item<ROWS, BF>(a, blockIdx.x, it)))
+  if (!(UP ? up_item<ROWS, BF, SPLIT>(a, blockIdx.x, it) : down_item<ROWS, BF, SPLIT>(a, blockIdx.x, it)))
     return;  // uniform for the whole block, before any barrier
-  ffn_run_item<UP, ROWS, BF>(a, it, smem);
+  ffn_run_item<UP, ROWS, BF, false, SPLIT>(a, it, smem);
+}
+
+// Split-K up-projection: g and u of each row summed over the slices in
+// order, then what the unsplit epilogue does with them: h = bf16(silu(bf16 g)
+// * bf16 u), the amax of each row's 128-column block, e4m3 h and its scale.
+// 32 threads per (row, h block), 4 columns each; R * I / 4 threads in all
+// (I a multiple of 128, so the 32 threads of a block are always all present).
+__global__ __launch_bounds__(256) void ffn_up_reduce_kernel(const float* __restrict__ part, int ks, int64_t R, int I,
+                                                            uint8_t* __restrict__ hq, float* __restrict__ hs) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 4-column chunk
+  const int nq = I / 4;
+  if (i >= R * nq) return;
+  const int64_t row = i / nq;
+  const int c = (int)(i - row * nq) * 4;
+  const size_t plane = (size_t)R * 2 * I;
+  const float* src = part + (size_t)row * 2 * I + c;
+  float gs[4] = {0.f, 0.f, 0.f, 0.f}, us[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < ks; ++k) {
+    const float4 gv = *(const float4*)(src + k * plane), uv = *(const float4*)(src + k * plane + I);
+    gs[0] += gv.x; gs[1] += gv.y; gs[2] += gv.z; gs[3] += gv.w;
+    us[0] += uv.x; us[1] += uv.y; us[2] += uv.z; us[3] += uv.w;
+  }
+  float h[4], amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float gv = round_bf16(gs[j]), uv = round_bf16(us[j]);
+    h[j] = round_bf16(gv / (1.f + expf(-gv)) * uv);
+    amax = fmaxf(amax, fabsf(h[j]));
+  }
+#pragma unroll
+  for (int o = 1; o < 32; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o));
+  const float sc = amax == 0.f ? 1.f : amax / E4M3_MAX;
+  *(uint32_t*)(hq + row * I + c) = pack4_e4m3(h[0] / sc, h[1] / sc, h[2] / sc, h[3] / sc);
+  if ((c & (BLK - 1)) == 0) hs[row * (I / BLK) + c / BLK] = sc;
+}
+
+// Split-K down-projection: out[r] = bf16(sum over slices k in order of
+// part[k][r]), 8 features per thread.
+__global__ __launch_bounds__(256) void ffn_reduce_kernel(const float* __restrict__ part, int ks, int64_t R, int d,
+                                                         uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 8-feature chunk
+  if (i >= R * (d / 8)) return;
+  const size_t plane = (size_t)R * d;
+  float y[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) y[j] = 0.f;
+  for (int k = 0; k < ks; ++k) {
+    const float4 lo = *(const float4*)(part + k * plane + 8 * i), hi = *(const float4*)(part + k * plane + 8 * i + 4);
+    y[0] += lo.x; y[1] += lo.y; y[2] += lo.z; y[3] += lo.w;
+    y[4] += hi.x; y[5] += hi.y; y[6] += hi.z; y[7] += hi.w;
+  }
+  uint4 o;
+  o.x = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+  o.y = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+  o.z = (uint32_t)f32_to_bf16(y[4]) | ((uint32_t)f32_to_bf16(y[5]) << 16);
+  o.w = (uint32_t)f32_to_bf16(y[6]) | ((uint32_t)f32_to_bf16(y[7]) << 16);
+  *(uint4*)(out + 8 * i) = o;
 }
 
 template <int ROWS, bool BF>
 hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
-  const int64_t g1 = max_tiles * (a.I / BLK);
-  const int64_t g2 = max_tiles * ((a.d / BLK + 1) / 2);
+  const int64_t R = (int64_t)a.T * a.K + a.T;
+  const int64_t g1 = max_tiles * items_per_tile(a.I / BLK, a.up_ks);
+  const int64_t g2 = max_tiles * items_per_tile((a.d / BLK + 1) / 2, a.dn_ks);
   if (ev) (void)hipEventRecord(ev[0], s);
-  hipLaunchKernelGGL((ffn_tiled_kernel<true, ROWS, BF>), dim3((unsigned)g1), dim3(512), 0, s, a);
+  if (!BF && a.up_ks > 1)
+    hipLaunchKernelGGL((ffn_tiled_kernel<true, ROWS, false, true>), dim3((unsigned)g1), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_tiled_kernel<true, ROWS, BF, false>), dim3((unsigned)g1), dim3(512), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (!BF && a.up_ks > 1) {
+    const int64_t chunks = R * (a.I / 4);
+    hipLaunchKernelGGL(ffn_up_reduce_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, a.part,
+                       a.up_ks, R, a.I, a.hq, a.hs);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   if (ev) (void)hipEventRecord(ev[1], s);
-  hipLaunchKernelGGL((ffn_tiled_kernel<false, ROWS, BF>), dim3((unsigned)g2), dim3(512), 0, s, a);
+  if (!BF && a.dn_ks > 1)
+    hipLaunchKernelGGL((ffn_tiled_kernel<false, ROWS, false, true>), dim3((unsigned)g2), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((ffn_tiled_kernel<false, ROWS, BF, false>), dim3((unsigned)g2), dim3(512), 0, s, a);
   err = hipGetLastError();
+  if (err == hipSuccess && !BF && a.dn_ks > 1) {
+    const int64_t chunks = R * (a.d / 8);
+    hipLaunchKernelGGL(ffn_reduce_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, a.part, a.dn_ks,
+                       R, a.d, a.out);
+    err = hipGetLastError();
+  }
   if (ev) (void)hipEventRecord(ev[2], s);
   return err;
 }
@@ -79,6 +160,44 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows) {
   return (T * K) / tile_rows + E + (T + tile_rows - 1) / tile_rows + 1;
 }
 
+namespace {
+
+// K slices of one projection: `items` items of nkb K blocks each, `slots`
+// workgroups resident at once, pbytes of fp32 partials per slice.  Cost
+// model, in units of one K block's time: the items run in rounds of `slots`,
+// each taking its K blocks plus about two blocks of start-up and epilogue;
+// the partial planes, written and read back, cost their bytes at the rate of
+// one round's weight stream (slots x 32 KiB per block time).  A split is
+// taken only when it beats the unsplit cost by 10 %.
+void pick_ksplit(int64_t items, int nkb, int slots, double pbytes, int* ks, int* kper) {
+  auto rounds = [&](int64_t n) { return (double)((n + slots - 1) / slots); };
+  const double unsplit = rounds(items) * (nkb + 2);
+  double best = unsplit * 0.9;
+  *ks = 1;
+  *kper = nkb;
+  for (int k = 2; k <= 16; ++k) {
+    const int per = (nkb + k - 1) / k;
+    if (per < 4) break;
+    const int kk = (nkb + per - 1) / per;  // no empty slice
+    const double cost = rounds(items * kk) * (per + 2) + kk * 2.0 * pbytes / (slots * 32768.0);
+    if (cost < best) {
+      best = cost;
+      *ks = kk;
+      *kper = per;
+    }
+  }
+}
+
+}  // namespace
+
+void ffn_dense_ksplit(int64_t T, int d, int I, int* up_ks, int* up_kper, int* dn_ks, int* dn_kper) {
+  const int NT = ffn_tile_rows(T);
+  const int slots = 256 * (NT == 32 ? Tile<32>::OCC : Tile<128>::OCC);
+  const int64_t tiles = (T + NT - 1) / NT;
+  pick_ksplit(tiles * (I / BLK), d / BLK, slots, (double)T * 2 * I * 4, up_ks, up_kper);
+  pick_ksplit(tiles * ((d / BLK + 1) / 2), I / BLK, slots, (double)T * d * 4, dn_ks, dn_kper);
+}
+
 int ffn_plan_cap(int64_t T, int K, int E, bool has_shared) {
   const int NT = ffn_tile_rows(T);
   return (int)(ffn_max_tiles(T, K, E, NT) - (has_shared ? (T + NT - 1) / NT : 0));
@@ -87,7 +206,7 @@ int ffn_plan_cap(int64_t T, int K, int E, bool has_shared) {
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E, int K,
                       const int32_t* offsets, const int32_t* row_token, const uint8_t* xq, const float* xs,
                       int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs, uint16_t* out, hipStream_t s,
-                      hipEvent_t* ev, bool bf16, int e_lo, int e_hi, bool planned) {
+                      hipEvent_t* ev, bool bf16, int e_lo, int e_hi, bool planned, const FfnSplit* split) {
   if (e_hi < 0) e_hi = E;
   const int NT = ffn_tile_rows(T);
   const int64_t max_tiles = ffn_max_tiles(T, K, E, NT);
@@ -114,6 +233,11 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
   a.hq = hq;
   a.hs = hs;
   a.out = out;
+  a.part = split ? split->part : nullptr;
+  a.up_ks = split && !bf16 ? split->up_ks : 1;  // split K: e4m3 only
+  a.up_kper = split ? split->up_kper : 0;
+  a.dn_ks = split && !bf16 ? split->dn_ks : 1;
+  a.dn_kper = split ? split->dn_kper : 0;
   if (NT == 32) return bf16 ? launch_gemms<32, true>(a, max_tiles, s, ev) : launch_gemms<32, false>(a, max_tiles, s, ev);
   return bf16 ? launch_gemms<128, true>(a, max_tiles, s, ev) : launch_gemms<128, false>(a, max_tiles, s, ev);
 }

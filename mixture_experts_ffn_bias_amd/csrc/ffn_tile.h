@@ -37,7 +37,22 @@ struct FfnArgs {
   uint8_t* hq;
   float* hs;
   uint16_t* out;
+  // Split K (a projection with too few items to occupy the chip): with
+  // up_ks / dn_ks > 1, item (tile, block, slice k) of that projection
+  // multiplies K blocks [k kper, k kper + kper) and stores fp32 partial rows
+  // in part[k][row][...] (rows T*K + T): up: [2 I], g then u; down: [d].
+  // The reduce kernels add the slices in order.
+  float* part;
+  int dn_ks, dn_kper;
+  int up_ks, up_kper;
 };
+
+// Items of one tile in a projection of nblk blocks: with split K (ks > 1) the
+// ks slices of a block are consecutive and the count is padded to a multiple
+// of 8, so that the items of the tiles of one expert, which read the same
+// weights, fall on the same XCD (workgroups are dealt to the eight XCDs in
+// turn) and share its L2.
+__host__ __device__ inline int items_per_tile(int nblk, int ks) { return ks > 1 ? (nblk * ks + 7) & ~7 : nblk; }
 
 // ---------------------------------------------------------------------------
 // LDS-tiled kernels.  A workgroup (8 waves) owns one tile of up to 128 rows
@@ -399,7 +414,27 @@ struct Item {
   int blk;             // up: the 128-wide h block; down: the pair of 128-feature output blocks
   int row0, nrows;     // the tile's permuted rows
   bool once;           // the tile is the only one of its expert
+  int nkb;             // K blocks multiplied
+  int kslice;          // K slice (split K), else 0
 };
+
+// Restrict an item to K slice k (K blocks [k kper, k kper + kper); the host
+// picks the slicing so that no slice is empty).
+template <int ROWS, bool BF>
+__device__ __forceinline__ void item_kslice(Item<ROWS>& it, int k, int kper) {
+  const int kb0 = k * kper;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) it.src.a[i] += kb0 * BLK;
+#pragma unroll
+  for (int j = 0; j < Tile<ROWS>::APW; ++j) it.src.b[j] += kb0 * BLK;
+  if (!BF) {
+    it.src.s += kb0;
+    it.sa0 += kb0;
+    it.sa1 += kb0;
+  }
+  it.nkb = min(kper, it.nkb - kb0);
+  it.kslice = k;
+}
 
 // Up-projection item of tile td (tile list entry: expert, first row, rows,
 // once) and h block ib.
@@ -433,16 +468,25 @@ __device__ __forceinline__ void up_item_of(const FfnArgs& a, int4 td, int ib, It
   it.row0 = row0;
   it.nrows = nrows;
   it.once = td.w != 0;
+  it.nkb = nkb;
+  it.kslice = 0;
 }
 
-// Item `item` of the up-projection (tile item / nib, h block item % nib);
-// false past the last tile.
-template <int ROWS, bool BF>
+// Item `item` of the up-projection (tile item / nib, h block item % nib;
+// with split K, tile item / items_per_tile, then h block and K slice); false
+// past the last tile and for padding items.  SPLIT: the kernel instance that
+// handles split K (a.up_ks is read only there).
+template <int ROWS, bool BF, bool SPLIT>
 __device__ __forceinline__ bool up_item(const FfnArgs& a, int item, Item<ROWS>& it) {
   const int nib = a.I / BLK;
-  const int tile = item / nib;
-  if (tile >= *a.n_tiles) return false;
-  up_item_of<ROWS, BF>(a, a.tiles[tile], item - tile * nib, it);
+  const int ks = SPLIT && a.up_ks > 1 ? a.up_ks : 1;
+  const int per_tile = items_per_tile(nib, ks);
+  const int tile = item / per_tile;
+  const int rem = item - tile * per_tile;
+  if (tile >= *a.n_tiles || rem >= nib * ks) return false;
+  const int ib = rem / ks;
+  up_item_of<ROWS, BF>(a, a.tiles[tile], ib, it);
+  if (ks > 1) item_kslice<ROWS, BF>(it, rem - ib * ks, a.up_kper);
   return true;
 }
 
@@ -470,16 +514,25 @@ __device__ __forceinline__ void down_item_of(const FfnArgs& a, int4 td, int ob, 
   it.row0 = row0;
   it.nrows = nrows;
   it.once = td.w != 0;
+  it.nkb = nkb;
+  it.kslice = 0;
 }
 
 // Item `item` of the down-projection (tile item / nob2, output blocks
-// 2 (item % nob2) and 2 (item % nob2) + 1); false past the last tile.
-template <int ROWS, bool BF>
+// 2 (item % nob2) and 2 (item % nob2) + 1; with split K, tile
+// item / items_per_tile, then output pair and K slice); false past the last
+// tile and for padding items.
+template <int ROWS, bool BF, bool SPLIT>
 __device__ __forceinline__ bool down_item(const FfnArgs& a, int item, Item<ROWS>& it) {
   const int nob2 = (a.d / BLK + 1) >> 1;
-  const int tile = item / nob2;
-  if (tile >= *a.n_tiles) return false;
-  down_item_of<ROWS, BF>(a, a.tiles[tile], item - tile * nob2, it);
+  const int ks = SPLIT && a.dn_ks > 1 ? a.dn_ks : 1;
+  const int per_tile = items_per_tile(nob2, ks);
+  const int tile = item / per_tile;
+  const int rem = item - tile * per_tile;
+  if (tile >= *a.n_tiles || rem >= nob2 * ks) return false;
+  const int ob = rem / ks;
+  down_item_of<ROWS, BF>(a, a.tiles[tile], ob, it);
+  if (ks > 1) item_kslice<ROWS, BF>(it, rem - ob * ks, a.dn_kper);
   return true;
 }
 
@@ -494,13 +547,34 @@ __device__ __forceinline__ int item_mvalid(const Item<ROWS>& it) {
 // columns of h block it.blk x its 64 rows; e4m3: per-row amax over the
 // block's 128 columns (4 waves) through `red` (2 KiB of LDS), then e4m3 h
 // and its scale; bf16: h itself.
-template <int ROWS, bool BF, bool COH>
+template <int ROWS, bool BF, bool COH, bool SPLIT>
 __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& it,
                                             const v4f (&acc)[2][2][Tile<ROWS>::MVMAX], float* red) {
   constexpr int MVX = Tile<ROWS>::MVMAX;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 15, g = lane >> 4;
   const int wr = wave >> 2, wc = wave & 3;
   const int nib = a.I / BLK;
+  if constexpr (SPLIT && !BF) {
+    if (a.up_ks > 1) {  // fp32 partials of g and u for K slice it.kslice
+      const size_t R = (size_t)a.T * a.K + a.T;
+#pragma unroll
+      for (int m = 0; m < MVX; ++m) {
+        const int rr = wr * 64 + 16 * m + r;
+        if (rr < it.nrows) {
+          float* prow = a.part + ((size_t)it.kslice * R + it.row0 + rr) * 2 * a.I;
+#pragma unroll
+          for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt) {
+              const v4f v = acc[gi][jt][m];
+              *(float4*)(prow + gi * a.I + it.blk * BLK + wc * 32 + jt * 16 + 4 * g) =
+                  make_float4(v[0], v[1], v[2], v[3]);
+            }
+        }
+      }
+      return;
+    }
+  }
   if constexpr (BF) {
 #pragma unroll
     for (int m = 0; m < MVX; ++m) {
@@ -564,7 +638,7 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
 
 // Down-projection epilogue: the wave's rows of output blocks 2 it.blk and
 // 2 it.blk + 1 (the second may lie past d), bf16.
-template <int ROWS, bool COH>
+template <int ROWS, bool COH, bool SPLIT>
 __device__ __forceinline__ void down_epilogue(const FfnArgs& a, const Item<ROWS>& it,
                                               const v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
   constexpr int MVX = Tile<ROWS>::MVMAX;
@@ -582,10 +656,16 @@ __device__ __forceinline__ void down_epilogue(const FfnArgs& a, const Item<ROWS>
 #pragma unroll
           for (int jt = 0; jt < 2; ++jt) {
             const v4f v = acc[gi][jt][m];
+            const size_t col = (size_t)(2 * it.blk + gi) * BLK + wc * 32 + jt * 16 + 4 * g;
+            if (SPLIT && a.dn_ks > 1) {  // fp32 partial of K slice it.kslice
+              const size_t R = (size_t)a.T * a.K + a.T;
+              *(float4*)(a.part + ((size_t)it.kslice * R + row) * a.d + col) = make_float4(v[0], v[1], v[2], v[3]);
+              continue;
+            }
             uint2 o;
             o.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
             o.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-            st8<COH>(a.out + row * a.d + (2 * it.blk + gi) * BLK + wc * 32 + jt * 16 + 4 * g, o);
+            st8<COH>(a.out + row * a.d + col, o);
           }
         }
       }
@@ -611,19 +691,19 @@ __device__ __forceinline__ void zero_acc(v4f (&acc)[2][2][Tile<ROWS>::MVMAX]) {
 // agent-coherent loads (common.h, ld / st).  Activation rows keep the plain
 // policy: every 128-byte line of them comes from one producer, complete
 // before any workgroup reads it; a line of scales spans two rows, which may
-// belong to tiles finished at different times.
-template <bool UP, int ROWS, bool BF, bool COH = false>
+// belong to tiles finished at different times.  SPLIT: the item may be a K
+// slice, whose epilogue stores fp32 partials (FfnArgs: up_ks, dn_ks).
+template <bool UP, int ROWS, bool BF, bool COH = false, bool SPLIT = false>
 __device__ __forceinline__ void ffn_run_item(const FfnArgs& a, const Item<ROWS>& it, uint8_t* smem) {
-  constexpr int EB = BF ? 2 : 1;
-  const int nkb = (UP ? a.d : a.I) * EB / BLK;
+  const int nkb = it.nkb;
   v4f acc[2][2][Tile<ROWS>::MVMAX];
   zero_acc<ROWS>(acc);
   run_mainloop<ROWS, BF, COH ? CPOL_SC1 : 0>(smem, it.src, it.sa0, it.sa1, nkb, it.nrows, item_mvalid(it), it.once,
                                              acc);
   if constexpr (UP)
-    up_epilogue<ROWS, BF, COH>(a, it, acc, (float*)smem);  // the stage buffers are no longer read
+    up_epilogue<ROWS, BF, COH, SPLIT>(a, it, acc, (float*)smem);  // the stage buffers are no longer read
   else
-    down_epilogue<ROWS, COH>(a, it, acc);
+    down_epilogue<ROWS, COH, SPLIT>(a, it, acc);
 }
 
 }  // namespace

@@ -58,11 +58,20 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
 // exactly those experts (expert e_lo first).  Rows of other experts are left
 // untouched.  planned: the tile list is already in tiles / n_tiles (written
 // by launch_permute with a PlanArgs), so no plan kernel runs.
+// split: NULL, or split K of the projections (ffn_dense_ksplit).
+struct FfnSplit {
+  float* part;  // max(up_ks * 2 I, dn_ks * d) * (T*K + T) fp32 partials
+  int up_ks, up_kper, dn_ks, dn_kper;
+};
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E,
                       int K, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
                       const float* xs, int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs,
                       uint16_t* out, hipStream_t s, hipEvent_t* ev = nullptr, bool bf16 = false,
-                      int e_lo = 0, int e_hi = -1, bool planned = false);
+                      int e_lo = 0, int e_hi = -1, bool planned = false, const FfnSplit* split = nullptr);
+// Split K of the dense MLP's projections (one expert over T rows, e4m3) for
+// batches with too few items to occupy the chip: slices of *_kper K blocks,
+// *_ks = 1 where splitting does not pay.
+void ffn_dense_ksplit(int64_t T, int d, int I, int* up_ks, int* up_kper, int* dn_ks, int* dn_kper);
 // routed tiles the plan may write (the tile list holds ffn_max_tiles entries)
 int ffn_plan_cap(int64_t T, int K, int E, bool has_shared);
 

@@ -546,6 +546,20 @@ def test_mlp_tiny(T):
     assert_rows_close(got, _mlp_ref(_np_params(p), f64(x)), f"mlp tiny T={T}")
 
 
+@pytest.mark.parametrize("T", [1, 37, 64, 128, 129, 300])
+def test_mlp_split_k(T):
+    # 17 K blocks into the up-projection and 13 into the down-projection, 13
+    # h blocks and a ragged last pair of output blocks: at these batch sizes
+    # both projections are split over K in slices of 4 blocks, the last one a
+    # single block, with 32-row tiles (T <= 128) and 128-row tiles
+    d, inter = 2176, 1664
+    _say(f"moe_mlp split K d={d} inter={inter} T={T}")
+    p = synth.mlp_weights(d, inter, DEV, seed=9)
+    x = synth.make_x(synth.Dims(d, 1, 1, 1, 1, inter), T, DEV, seed=90 + T)
+    got = f64(run_mlp(p, x, d, inter))
+    assert_rows_close(got, _mlp_ref(_np_params(p), f64(x)), f"mlp split K T={T}")
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("T", [64, 1000])
 def test_mlp_full_width_sampled_rows(T):
