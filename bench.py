@@ -225,6 +225,8 @@ def main():
     ap.add_argument("--mlp", type=int, default=0, metavar="INTER",
                     help="time the dense SwiGLU MLP of the blocks before the MoE blocks instead (moe_mlp, FP8 "
                          "weights d_model -> INTER -> d_model, e.g. 18432) over the workload's tokens")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="with --mlp: the batch's token count (default: the workload's)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -516,7 +518,7 @@ def bench_mlp(args, moe, synth, torch, np, dev):
     d, inter = wl.dims.d_model, args.mlp
     if args.weights != "e4m3":
         sys.exit("--mlp takes e4m3 weights")
-    T = wl.tokens
+    T = args.tokens or wl.tokens
     x = synth.make_x(wl.dims, T, dev, wl.seed)
     p = synth.mlp_weights(d, inter, dev, wl.seed)
     mlp = moe.experts_struct(*(p[k] for k in ("w1", "w3", "w2", "s1", "s3", "s2")))

@@ -113,7 +113,7 @@ MlpLayout mlp_layout(int d, int I, int64_t T) {
   const size_t t = (size_t)T;
   L.xq = take(t * d);
   L.xs = take(t * (d / BLK) * 4);
-  L.tiles = take((size_t)ffn_max_tiles(T, 0, 0, ffn_tile_rows(T)) * sizeof(int4));
+  L.tiles = take((size_t)ffn_max_tiles(T, 0, 0, ffn_tile_rows(T, true)) * sizeof(int4));
   L.n_tiles = take(4);
   L.hq = take(t * I);
   L.hs = take(t * (I / BLK) * 4);

@@ -150,9 +150,12 @@ hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipE
 
 }  // namespace
 
-int ffn_tile_rows(int64_t T) {
+int ffn_tile_rows(int64_t T, bool dense) {
   // small batches: experts hold a few rows each and the weights are the
-  // traffic; narrow tiles let two workgroups share a CU
+  // traffic; narrow tiles let two workgroups share a CU.  A dense MLP of
+  // 33..128 rows streams the same weights for every tile: 64-row tiles cut
+  // the workgroups that stream each weight byte to one or two.
+  if (dense && T > 32 && T <= 128) return 64;
   return T <= 128 ? 32 : 128;
 }
 
@@ -191,8 +194,8 @@ void pick_ksplit(int64_t items, int nkb, int slots, double pbytes, int* ks, int*
 }  // namespace
 
 void ffn_dense_ksplit(int64_t T, int d, int I, int* up_ks, int* up_kper, int* dn_ks, int* dn_kper) {
-  const int NT = ffn_tile_rows(T);
-  const int slots = 256 * (NT == 32 ? Tile<32>::OCC : Tile<128>::OCC);
+  const int NT = ffn_tile_rows(T, true);
+  const int slots = 256 * (NT == 32 ? Tile<32>::OCC : NT == 64 ? Tile<64>::OCC : Tile<128>::OCC);
   const int64_t tiles = (T + NT - 1) / NT;
   pick_ksplit(tiles * (I / BLK), d / BLK, slots, (double)T * 2 * I * 4, up_ks, up_kper);
   pick_ksplit(tiles * ((d / BLK + 1) / 2), I / BLK, slots, (double)T * d * 4, dn_ks, dn_kper);
@@ -208,7 +211,8 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
                       int4* tiles, int32_t* n_tiles, uint8_t* hq, float* hs, uint16_t* out, hipStream_t s,
                       hipEvent_t* ev, bool bf16, int e_lo, int e_hi, bool planned, const FfnSplit* split) {
   if (e_hi < 0) e_hi = E;
-  const int NT = ffn_tile_rows(T);
+  const bool dense = K == 0;  // one dense expert (the MLP)
+  const int NT = ffn_tile_rows(T, dense);
   const int64_t max_tiles = ffn_max_tiles(T, K, E, NT);
   const int nsh = shared ? (T + NT - 1) / NT : 0;
   if (!planned) {
@@ -239,6 +243,7 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
   a.dn_ks = split && !bf16 ? split->dn_ks : 1;
   a.dn_kper = split ? split->dn_kper : 0;
   if (NT == 32) return bf16 ? launch_gemms<32, true>(a, max_tiles, s, ev) : launch_gemms<32, false>(a, max_tiles, s, ev);
+  if (NT == 64) return bf16 ? hipErrorInvalidValue : launch_gemms<64, false>(a, max_tiles, s, ev);
   return bf16 ? launch_gemms<128, true>(a, max_tiles, s, ev) : launch_gemms<128, false>(a, max_tiles, s, ev);
 }
 

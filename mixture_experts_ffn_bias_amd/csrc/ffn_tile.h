@@ -94,17 +94,21 @@ constexpr int CPOL_SC1 = 16;                 // ... of an agent-coherent load (c
 //   ROWS = 32 (small batches, where the weights are the traffic): two stages
 //     of 36 KiB and at most 128 VGPRs, so two workgroups share a CU and one's
 //     start-up and epilogue overlap the other's weight stream.
+//   ROWS = 64 (a dense MLP of 33..128 rows): one workgroup per CU with three
+//     stages (121 KiB), so two K blocks of weights are in flight per CU and
+//     each weight byte is streamed by at most two workgroups; only the
+//     first row of waves multiplies (as with 32 rows).
 template <int ROWS>
 struct Tile {
-  static_assert(ROWS == 32 || ROWS == 128, "tile rows");
+  static_assert(ROWS == 32 || ROWS == 64 || ROWS == 128, "tile rows");
   static constexpr int B_BYTES = ROWS * BLK;
   static constexpr int S_BYTES = ROWS * 4;
   static constexpr int STAGE = TT_A_BYTES + B_BYTES + S_BYTES;
   template <bool BF>
-  static constexpr int NSTAGE = ROWS == 128 && BF ? 3 : 2;
+  static constexpr int NSTAGE = ROWS == 64 || (ROWS == 128 && BF) ? 3 : 2;
   template <bool BF>
   static constexpr int SMEM = NSTAGE<BF> * STAGE;
-  static constexpr int OCC = ROWS == 128 ? 1 : 2;       // workgroups per CU (8 waves each: 2 OCC waves per SIMD)
+  static constexpr int OCC = ROWS == 32 ? 2 : 1;        // workgroups per CU (8 waves each: 2 OCC waves per SIMD)
   static constexpr int APW = ROWS == 128 ? 2 : 1;       // 8-row activation pieces per copying wave
   static constexpr int AWAVES = ROWS / (8 * APW);       // waves that copy activation rows
   static constexpr int SWAVES = (ROWS + 63) / 64;       // waves that copy activation scales (64 rows each)

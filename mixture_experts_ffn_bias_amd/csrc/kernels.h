@@ -45,7 +45,7 @@ hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, i
 hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s);
 
 // ffn.hip
-int ffn_tile_rows(int64_t T);                       // rows per FFN tile for this token count
+int ffn_tile_rows(int64_t T, bool dense = false);   // rows per FFN tile for this token count (dense: the MLP)
 int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
 // E = K = 0 with `shared` set and row_token NULL runs one dense expert over
 // rows 0..T-1 (offsets is then not read).
