@@ -291,7 +291,11 @@ size_t moe_mlp_workspace_size(int32_t d_model, int32_t inter, int64_t tokens);
  *   x     bf16 [T][d_model] (16-byte aligned)
  *   out   bf16 [T][d_model] out (16-byte aligned; must not alias x)
  * d_model and inter: multiples of 128, at most 32768.  Needs
- * moe_mlp_workspace_size(d_model, inter, T) bytes of workspace (256-byte aligned). */
+ * moe_mlp_workspace_size(d_model, inter, T) bytes of workspace (256-byte aligned).
+ * The workspace holds Q(x), the tile list, Q(h) and, for batches too small
+ * to occupy the GPU, fp32 partial sums of the two products over slices of
+ * their K range.  The partials are added in a fixed order, so repeated calls
+ * give identical results.  Its contents are scratch between calls. */
 int moe_mlp(int32_t d_model, int32_t inter, int64_t tokens, const moe_experts* mlp, const uint16_t* x,
             uint16_t* out, void* workspace, size_t workspace_bytes, void* stream);
 

@@ -556,8 +556,11 @@ def test_mlp_split_k(T):
     _say(f"moe_mlp split K d={d} inter={inter} T={T}")
     p = synth.mlp_weights(d, inter, DEV, seed=9)
     x = synth.make_x(synth.Dims(d, 1, 1, 1, 1, inter), T, DEV, seed=90 + T)
-    got = f64(run_mlp(p, x, d, inter))
+    first = run_mlp(p, x, d, inter)
+    got = f64(first)
     assert_rows_close(got, _mlp_ref(_np_params(p), f64(x)), f"mlp split K T={T}")
+    # the slices' partial sums are added in a fixed order: a second call is bit-identical
+    assert torch.equal(run_mlp(p, x, d, inter), first)
 
 
 @pytest.mark.slow
