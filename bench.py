@@ -79,10 +79,19 @@ KERNEL_SOURCES = tuple("mixture_experts_ffn_bias_amd/csrc/" + f for f in ("ffn.h
 
 
 def kernel_source_digest() -> str:
+    """SHA-256 of the FFN kernel sources' code.
+
+    Comments are removed and whitespace collapsed first, so that an edit of a
+    comment leaves the digest, and the counters taken with the same code,
+    valid.  (None of these sources has a comment marker inside a string.)
+    """
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        src = open(os.path.join(ROOT, f)).read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

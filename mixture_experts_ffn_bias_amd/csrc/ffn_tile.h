@@ -63,16 +63,17 @@ __host__ __device__ inline int items_per_tile(int nblk, int ks) { return ks > 1 
 //   down-projection: two consecutive 128-feature blocks of w2.
 // Per 128-deep K block, the e4m3 weight (256 x 128 B) and activation
 // (128 x 128 B) tiles and the activation scales are copied global -> LDS
-// directly (global_load_lds, no register staging) into one of two stage
-// buffers, one K block ahead of the multiply.  Rows are stored unpadded with
-// their 16-byte chunks XOR-permuted (swz), which makes the MFMA-layout reads
-// bank-conflict free.  Wave (wr, wc) multiplies rows [64 wr, 64 wr + 64) by
-// weight rows {32 wc .. 32 wc + 31} of both groups: 4 x 4 block products per
-// K block.
-// The weight copies of a tile that is the only one of its expert (every tile
-// when T <= 128) carry the non-temporal hint: those bytes are read exactly
-// once, and full-line DMA streams with the hint reach a markedly higher HBM
-// read rate on gfx950 (about 7.0 against 6.2 TB/s in a plain read test).
+// directly (global_load_lds, no register staging) into one of the NSTAGE
+// stage buffers (Tile below), NSTAGE - 1 K blocks ahead of the multiply.
+// Rows are stored unpadded with their 16-byte chunks XOR-permuted (swz),
+// which makes the MFMA-layout reads bank-conflict free.  Wave (wr, wc)
+// multiplies rows [64 wr, 64 wr + 64) by weight rows {32 wc .. 32 wc + 31}
+// of both groups: 4 x 4 block products per K block.
+// The weight copies of a tile that is the only one of its expert (at decode
+// sizes, nearly every routed expert's) carry the non-temporal hint: those
+// bytes are read exactly once, and full-line DMA streams with the hint reach
+// a markedly higher HBM read rate on gfx950 (about 7.0 against 6.2 TB/s in a
+// plain read test).
 // Weights that other tiles read again are loaded with the default policy so
 // that the L2 can serve the repeat reads.
 // ---------------------------------------------------------------------------
