@@ -542,14 +542,16 @@ int moe_mlp(int32_t d_model, int32_t inter, int64_t tokens, const moe_experts* m
   const hipStream_t s = (hipStream_t)stream;
   uint8_t* xq = at<uint8_t>(workspace, L.xq);
   float* xs = at<float>(workspace, L.xs);
-  MOE_TRY(hip_status(launch_quant(x, tokens, d_model, xq, xs, s)));
-  // one dense expert: no routed experts, rows are tokens
+  // one dense expert: no routed experts, rows are tokens; the quantisation
+  // launch also writes its tile list
+  const PlanArgs plan{at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
+                      ffn_tile_rows(tokens, true), 1, 0};
+  MOE_TRY(hip_status(launch_quant(x, tokens, d_model, xq, xs, s, &plan)));
   const ExpertPtrs p = ptrs(*mlp);
   const FfnSplit split{at<float>(workspace, L.part), L.up_ks, L.up_kper, L.dn_ks, L.dn_kper};
-  return hip_status(launch_ffn(p, &p, (int)tokens, d_model, inter, 0, 0, nullptr, nullptr, xq, xs,
-                               at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
-                               at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), out, s, nullptr, false, 0,
-                               -1, false, &split));
+  return hip_status(launch_ffn(p, &p, (int)tokens, d_model, inter, 0, 0, nullptr, nullptr, xq, xs, plan.tiles,
+                               plan.n_tiles, at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), out, s, nullptr,
+                               false, 0, -1, true, &split));
 }
 
 const char* moe_status_string(int status) {

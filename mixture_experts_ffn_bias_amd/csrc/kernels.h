@@ -41,8 +41,12 @@ hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, i
                           int32_t* chunk_cnt, int32_t* chunk_off, int32_t* counts, int32_t* offsets,
                           int32_t* row_token, int32_t* pair_row, uint8_t* xq, float* xs, hipStream_t s,
                           const PlanArgs* plan = nullptr, bool* planned = nullptr);
-// per-128-block e4m3 quantisation of T rows of d bf16 values
-hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s);
+// per-128-block e4m3 quantisation of T rows of d bf16 values.  dense_plan
+// (may be NULL): also write the tile list of one dense expert over the T
+// rows (the MLP; tiles, n_tiles and tile_rows are read), as launch_ffn's
+// `planned` expects it.
+hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s,
+                        const PlanArgs* dense_plan = nullptr);
 
 // ffn.hip
 int ffn_tile_rows(int64_t T, bool dense = false);   // rows per FFN tile for this token count (dense: the MLP)

@@ -80,9 +80,19 @@ __global__ __launch_bounds__(PERM_CHUNK) void scatter_kernel(const int32_t* __re
   row_token[(size_t)T * K + t] = t;  // the shared expert's rows: identity
 }
 
+// plan.tiles (may be NULL): also write the FFN tile list of one dense
+// expert over the T rows (the MLP: tiles of plan.tile_rows rows, no routed
+// experts), so that no plan kernel runs; T * d / 16 threads cover its
+// ceil(T / tile_rows) entries.
 __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restrict__ x, int64_t nblocks,
-                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale,
+                                                         PlanArgs plan, int T) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (plan.tiles) {
+    const int nsh = (T + plan.tile_rows - 1) / plan.tile_rows;
+    if (gid < nsh) st16<false>(plan.tiles + gid, shared_tile((int)gid, T, 0, plan.tile_rows, nsh, 0));
+    if (gid == 0) *plan.n_tiles = nsh;
+  }
   const int64_t blk = gid >> 3;
   if (blk >= nblocks) return;  // whole 8-lane groups leave together
   quant_block(x, blk, (int)(gid & 7), q, scale);
@@ -107,10 +117,13 @@ __global__ __launch_bounds__(PERM_CHUNK) void permute_small_kernel(
 
 }  // namespace
 
-hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s) {
+hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s,
+                        const PlanArgs* dense_plan) {
   const int64_t nblocks = T * (d / BLK);
   const int64_t threads = nblocks * 8;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, nblocks, xq, xs);
+  const PlanArgs pa = dense_plan ? *dense_plan : PlanArgs{nullptr, nullptr, 0, 0, 0};
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, x, nblocks, xq, xs,
+                     pa, (int)T);
   return hipGetLastError();
 }
 

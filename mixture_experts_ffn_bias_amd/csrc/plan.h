@@ -10,6 +10,12 @@
 
 namespace moe {
 
+// Tile j of the shared expert (number e_sh, permuted rows [TK, TK + T), nsh
+// tiles): NT rows each in row order, the last one ragged.
+__device__ __forceinline__ uint4 shared_tile(int j, int T, int TK, int NT, int nsh, int e_sh) {
+  return make_uint4(e_sh, TK + j * NT, min(NT, T - j * NT), nsh == 1 ? 1 : 0);
+}
+
 // Thread e (0..255) brings expert e's permuted rows [lo, lo + cnt) (ignored
 // outside [e_lo, e_hi)); threads from 256 on only join the barriers.  s is
 // 256 ints of LDS.  Routed experts [e_lo, e_hi)
@@ -29,7 +35,7 @@ __device__ __forceinline__ void plan_tiles_block(int lo, int cnt, int T, int K, 
   const int TK = T * K;
   const int nsh = has_shared ? (T + NT - 1) / NT : 0;
   for (int j = threadIdx.x; j < nsh; j += blockDim.x)
-    st16<COH>(tiles + j, make_uint4(e_hi - e_lo, TK + j * NT, min(NT, T - j * NT), nsh == 1 ? 1 : 0));
+    st16<COH>(tiles + j, shared_tile(j, T, TK, NT, nsh, e_hi - e_lo));
   const int n = (act && e >= e_lo && e < e_hi) ? (cnt + NT - 1) / NT : 0;
   if (act) s[e] = n;
   __syncthreads();
