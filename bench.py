@@ -242,8 +242,8 @@ def main():
                     help="only run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this MoE layer build has no multi-GPU path "
-              "(run with --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU only: the layer runs on a single GPU here, and a rank's expert "
+              "share on one GPU is timed with --ep-share N (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
