@@ -100,6 +100,7 @@ FusedLayout fused_layout(const moe_dims& dm, int64_t T) {
 struct MlpLayout {
   size_t xq, xs, tiles, n_tiles, hq, hs, part, total;
   int up_ks, up_kper, dn_ks, dn_kper;  // split K (part: the larger set of fp32 partial planes)
+  int up_stream, up_planes;            // stream-K up-projection (ffn_dense_ksplit)
 };
 
 MlpLayout mlp_layout(int d, int I, int64_t T) {
@@ -117,8 +118,8 @@ MlpLayout mlp_layout(int d, int I, int64_t T) {
   L.n_tiles = take(4);
   L.hq = take(t * I);
   L.hs = take(t * (I / BLK) * 4);
-  ffn_dense_ksplit(T, d, I, &L.up_ks, &L.up_kper, &L.dn_ks, &L.dn_kper);
-  const size_t up_part = L.up_ks > 1 ? (size_t)L.up_ks * t * 2 * I * 4 : 0;
+  ffn_dense_ksplit(T, d, I, &L.up_ks, &L.up_kper, &L.dn_ks, &L.dn_kper, &L.up_stream, &L.up_planes);
+  const size_t up_part = (size_t)L.up_planes * t * 2 * I * 4;
   const size_t dn_part = L.dn_ks > 1 ? (size_t)L.dn_ks * t * d * 4 : 0;
   L.part = take(std::max(up_part, dn_part));
   L.total = off;
@@ -548,7 +549,7 @@ int moe_mlp(int32_t d_model, int32_t inter, int64_t tokens, const moe_experts* m
                       ffn_tile_rows(tokens, true), 1, 0};
   MOE_TRY(hip_status(launch_quant(x, tokens, d_model, xq, xs, s, &plan)));
   const ExpertPtrs p = ptrs(*mlp);
-  const FfnSplit split{at<float>(workspace, L.part), L.up_ks, L.up_kper, L.dn_ks, L.dn_kper};
+  const FfnSplit split{at<float>(workspace, L.part), L.up_ks, L.up_kper, L.dn_ks, L.dn_kper, L.up_stream};
   return hip_status(launch_ffn(p, &p, (int)tokens, d_model, inter, 0, 0, nullptr, nullptr, xq, xs, plan.tiles,
                                plan.n_tiles, at<uint8_t>(workspace, L.hq), at<float>(workspace, L.hs), out, s, nullptr,
                                false, 0, -1, true, &split));

@@ -56,18 +56,45 @@ __global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_tiled_kernel(Ffn
   ffn_run_item<UP, ROWS, BF, false, SPLIT>(a, it, smem);
 }
 
+// Stream-K up-projection of one dense expert (e4m3; FfnArgs::up_stream = L):
+// workgroup b runs units [b L, b L + L) of tiles x h blocks x K blocks,
+// segment by segment, each segment's partials into plane b - first(s).
+// Grid: ceil(units / L).
+template <int ROWS>
+__global__ __launch_bounds__(512, 2 * Tile<ROWS>::OCC) void ffn_stream_up_kernel(FfnArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[Tile<ROWS>::template SMEM<false>];
+  const int nib = a.I / BLK, nkb = a.d / BLK, L = a.up_stream;
+  const int64_t units = (int64_t)*a.n_tiles * nib * nkb;
+  int64_t u = (int64_t)blockIdx.x * L;
+  const int64_t u1 = min(u + L, units);
+  while (u < u1) {  // uniform for the whole block
+    const int s = (int)(u / nkb), kb0 = (int)(u - (int64_t)s * nkb);
+    const int n = (int)min(u1 - u, (int64_t)(nkb - kb0));
+    const int tile = s / nib;
+    Item<ROWS> it;
+    up_item_of<ROWS, false>(a, a.tiles[tile], s - tile * nib, it);
+    item_krange<ROWS, false>(it, kb0, n, (int)blockIdx.x - stream_first(s, nkb, L));
+    ffn_run_item<true, ROWS, false, false, true>(a, it, smem);
+    u += n;
+  }
+}
+
 // Split-K up-projection: g and u of each row summed over the slices in
 // order, then what the unsplit epilogue does with them: h = bf16(silu(bf16 g)
 // * bf16 u), the amax of each row's 128-column block, e4m3 h and its scale.
 // 32 threads per (row, h block), 4 columns each; R * I / 4 threads in all
 // (I a multiple of 128, so the 32 threads of a block are always all present).
+// Stream-K (L > 0, one dense expert in tiles of NT rows, nkb K blocks):
+// segment (tile, h block) s has stream_planes(s) planes instead of ks.
 __global__ __launch_bounds__(256) void ffn_up_reduce_kernel(const float* __restrict__ part, int ks, int64_t R, int I,
-                                                            uint8_t* __restrict__ hq, float* __restrict__ hs) {
+                                                            int L, int nkb, int NT, uint8_t* __restrict__ hq,
+                                                            float* __restrict__ hs) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;  // 4-column chunk
   const int nq = I / 4;
   if (i >= R * nq) return;
   const int64_t row = i / nq;
   const int c = (int)(i - row * nq) * 4;
+  if (L > 0) ks = stream_planes((int)(row / NT) * (I / BLK) + c / BLK, nkb, L);
   const size_t plane = (size_t)R * 2 * I;
   const float* src = part + (size_t)row * 2 * I + c;
   float gs[4] = {0.f, 0.f, 0.f, 0.f}, us[4] = {0.f, 0.f, 0.f, 0.f};
@@ -116,19 +143,28 @@ __global__ __launch_bounds__(256) void ffn_reduce_kernel(const float* __restrict
 template <int ROWS, bool BF>
 hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipEvent_t* ev) {
   const int64_t R = (int64_t)a.T * a.K + a.T;
-  const int64_t g1 = max_tiles * items_per_tile(a.I / BLK, a.up_ks);
+  // stream-K: one dense expert, ceil(T / ROWS) tiles, runs of up_stream units
+  const int64_t g1 = a.up_stream > 0
+                         ? ((int64_t)(a.T + ROWS - 1) / ROWS * (a.I / BLK) * (a.d / BLK) + a.up_stream - 1) / a.up_stream
+                         : max_tiles * items_per_tile(a.I / BLK, a.up_ks);
   const int64_t g2 = max_tiles * items_per_tile((a.d / BLK + 1) / 2, a.dn_ks);
   if (ev) (void)hipEventRecord(ev[0], s);
-  if (!BF && a.up_ks > 1)
+  if (!BF && a.up_stream > 0) {
+    if constexpr (ROWS == 32)
+      return hipErrorInvalidValue;  // the host picks stream-K for 64- and 128-row tiles only
+    else
+      hipLaunchKernelGGL(ffn_stream_up_kernel<ROWS>, dim3((unsigned)g1), dim3(512), 0, s, a);
+  } else if (!BF && a.up_ks > 1) {
     hipLaunchKernelGGL((ffn_tiled_kernel<true, ROWS, false, true>), dim3((unsigned)g1), dim3(512), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((ffn_tiled_kernel<true, ROWS, BF, false>), dim3((unsigned)g1), dim3(512), 0, s, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  if (!BF && a.up_ks > 1) {
+  if (!BF && (a.up_ks > 1 || a.up_stream > 0)) {
     const int64_t chunks = R * (a.I / 4);
     hipLaunchKernelGGL(ffn_up_reduce_kernel, dim3((unsigned)((chunks + 255) / 256)), dim3(256), 0, s, a.part,
-                       a.up_ks, R, a.I, a.hq, a.hs);
+                       a.up_ks, R, a.I, a.up_stream, a.d / BLK, ROWS, a.hq, a.hs);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -171,8 +207,9 @@ namespace {
 // each taking its K blocks plus about two blocks of start-up and epilogue;
 // the partial planes, written and read back, cost their bytes at the rate of
 // one round's weight stream (slots x 32 KiB per block time).  A split is
-// taken only when it beats the unsplit cost by 10 %.
-void pick_ksplit(int64_t items, int nkb, int slots, double pbytes, int* ks, int* kper) {
+// taken only when it beats the unsplit cost by 10 %.  Returns the cost of
+// the choice.
+double pick_ksplit(int64_t items, int nkb, int slots, double pbytes, int* ks, int* kper) {
   auto rounds = [&](int64_t n) { return (double)((n + slots - 1) / slots); };
   const double unsplit = rounds(items) * (nkb + 2);
   double best = unsplit * 0.9;
@@ -189,15 +226,44 @@ void pick_ksplit(int64_t items, int nkb, int slots, double pbytes, int* ks, int*
       *kper = per;
     }
   }
+  return *ks == 1 ? unsplit : best;
+}
+
+// Stream-K alternative, same units: `units` K blocks in runs of
+// L = max(4, ceil(units / slots)), one run per workgroup; a run crosses up to
+// ceil(L / nkb) + 1 segments (tile, block), each with its own start-up;
+// *planes: the most runs that share one segment.
+double stream_cost(int64_t units, int nkb, int slots, double pbytes, int* L, int* planes) {
+  const int l = (int)std::max<int64_t>(4, (units + slots - 1) / slots);
+  const int64_t runs = (units + l - 1) / l;
+  int np = 1;
+  for (int64_t sg = 0; sg < units / nkb; ++sg) np = std::max(np, stream_planes((int)sg, nkb, l));
+  *L = l;
+  *planes = np;
+  const int segs = (l + nkb - 1) / nkb + 1;
+  return (double)((runs + slots - 1) / slots) * (l + 2 * segs) + np * 2.0 * pbytes / (slots * 32768.0);
 }
 
 }  // namespace
 
-void ffn_dense_ksplit(int64_t T, int d, int I, int* up_ks, int* up_kper, int* dn_ks, int* dn_kper) {
+void ffn_dense_ksplit(int64_t T, int d, int I, int* up_ks, int* up_kper, int* dn_ks, int* dn_kper, int* up_stream,
+                      int* up_planes) {
   const int NT = ffn_tile_rows(T, true);
   const int slots = 256 * (NT == 32 ? Tile<32>::OCC : NT == 64 ? Tile<64>::OCC : Tile<128>::OCC);
   const int64_t tiles = (T + NT - 1) / NT;
-  pick_ksplit(tiles * (I / BLK), d / BLK, slots, (double)T * 2 * I * 4, up_ks, up_kper);
+  const double up_bytes = (double)T * 2 * I * 4;  // one plane of up-projection partials
+  const double sliced = pick_ksplit(tiles * (I / BLK), d / BLK, slots, up_bytes, up_ks, up_kper);
+  *up_planes = *up_ks > 1 ? *up_ks : 0;
+  *up_stream = 0;
+  int L = 0, np = 0;
+  // stream-K only where it beats the best slicing by 5 % (and not with
+  // 32-row tiles, whose single-row batches gain nothing from it)
+  if (NT != 32 && stream_cost(tiles * (I / BLK) * (d / BLK), d / BLK, slots, up_bytes, &L, &np) < 0.95 * sliced) {
+    *up_stream = L;
+    *up_planes = np;
+    *up_ks = 1;
+    *up_kper = d / BLK;
+  }
   pick_ksplit(tiles * ((d / BLK + 1) / 2), I / BLK, slots, (double)T * d * 4, dn_ks, dn_kper);
 }
 
@@ -242,6 +308,7 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
   a.up_kper = split ? split->up_kper : 0;
   a.dn_ks = split && !bf16 ? split->dn_ks : 1;
   a.dn_kper = split ? split->dn_kper : 0;
+  a.up_stream = split && !bf16 ? split->up_stream : 0;
   if (NT == 32) return bf16 ? launch_gemms<32, true>(a, max_tiles, s, ev) : launch_gemms<32, false>(a, max_tiles, s, ev);
   if (NT == 64) return bf16 ? hipErrorInvalidValue : launch_gemms<64, false>(a, max_tiles, s, ev);
   return bf16 ? launch_gemms<128, true>(a, max_tiles, s, ev) : launch_gemms<128, false>(a, max_tiles, s, ev);

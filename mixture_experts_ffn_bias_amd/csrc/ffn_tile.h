@@ -45,7 +45,18 @@ struct FfnArgs {
   float* part;
   int dn_ks, dn_kper;
   int up_ks, up_kper;
+  // Stream-K up-projection of one dense expert (up_stream = L > 0): the
+  // tiles x h blocks x K blocks units, in that order, are dealt in runs of L
+  // to the workgroups; a run covers one or more (tile, h block) segments,
+  // and workgroup b stores its part of segment s in partial plane
+  // b - first(s), first(s) = s nkb / L (stream_first).
+  int up_stream;
 };
+
+__host__ __device__ inline int stream_first(int s, int nkb, int L) { return (int)((int64_t)s * nkb / L); }
+__host__ __device__ inline int stream_planes(int s, int nkb, int L) {
+  return (int)(((int64_t)(s + 1) * nkb - 1) / L) - stream_first(s, nkb, L) + 1;
+}
 
 // Items of one tile in a projection of nblk blocks: with split K (ks > 1) the
 // ks slices of a block are consecutive and the count is padded to a multiple
@@ -423,11 +434,10 @@ struct Item {
   int kslice;          // K slice (split K), else 0
 };
 
-// Restrict an item to K slice k (K blocks [k kper, k kper + kper); the host
-// picks the slicing so that no slice is empty).
+// Restrict an item to K blocks [kb0, kb0 + n) (n >= 1), its partials going
+// to plane `plane`.
 template <int ROWS, bool BF>
-__device__ __forceinline__ void item_kslice(Item<ROWS>& it, int k, int kper) {
-  const int kb0 = k * kper;
+__device__ __forceinline__ void item_krange(Item<ROWS>& it, int kb0, int n, int plane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) it.src.a[i] += kb0 * BLK;
 #pragma unroll
@@ -437,8 +447,16 @@ __device__ __forceinline__ void item_kslice(Item<ROWS>& it, int k, int kper) {
     it.sa0 += kb0;
     it.sa1 += kb0;
   }
-  it.nkb = min(kper, it.nkb - kb0);
-  it.kslice = k;
+  it.nkb = n;
+  it.kslice = plane;
+}
+
+// Restrict an item to K slice k (K blocks [k kper, k kper + kper); the host
+// picks the slicing so that no slice is empty).
+template <int ROWS, bool BF>
+__device__ __forceinline__ void item_kslice(Item<ROWS>& it, int k, int kper) {
+  const int kb0 = k * kper;
+  item_krange<ROWS, BF>(it, kb0, min(kper, it.nkb - kb0), k);
 }
 
 // Up-projection item of tile td (tile list entry: expert, first row, rows,
@@ -560,7 +578,7 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
   const int wr = wave >> 2, wc = wave & 3;
   const int nib = a.I / BLK;
   if constexpr (SPLIT && !BF) {
-    if (a.up_ks > 1) {  // fp32 partials of g and u for K slice it.kslice
+    if (a.up_ks > 1 || a.up_stream > 0) {  // fp32 partials of g and u for K slice (plane) it.kslice
       const size_t R = (size_t)a.T * a.K + a.T;
 #pragma unroll
       for (int m = 0; m < MVX; ++m) {

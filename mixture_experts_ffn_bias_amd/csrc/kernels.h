@@ -64,8 +64,9 @@ int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
 // by launch_permute with a PlanArgs), so no plan kernel runs.
 // split: NULL, or split K of the projections (ffn_dense_ksplit).
 struct FfnSplit {
-  float* part;  // max(up_ks * 2 I, dn_ks * d) * (T*K + T) fp32 partials
+  float* part;  // max(up planes * 2 I, dn_ks * d) * (T*K + T) fp32 partials
   int up_ks, up_kper, dn_ks, dn_kper;
+  int up_stream;  // > 0: stream-K up-projection in runs of up_stream K blocks (one dense expert), up_ks ignored
 };
 hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T, int d, int I, int E,
                       int K, const int32_t* offsets, const int32_t* row_token, const uint8_t* xq,
@@ -75,7 +76,11 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
 // Split K of the dense MLP's projections (one expert over T rows, e4m3) for
 // batches with too few items to occupy the chip: slices of *_kper K blocks,
 // *_ks = 1 where splitting does not pay.
-void ffn_dense_ksplit(int64_t T, int d, int I, int* up_ks, int* up_kper, int* dn_ks, int* dn_kper);
+// *up_stream > 0 instead selects the stream-K up-projection (runs of
+// *up_stream K blocks; *up_ks = 1); *up_planes: the partial planes it needs
+// (the up-projection's, either way).
+void ffn_dense_ksplit(int64_t T, int d, int I, int* up_ks, int* up_kper, int* dn_ks, int* dn_kper, int* up_stream,
+                      int* up_planes);
 // routed tiles the plan may write (the tile list holds ffn_max_tiles entries)
 int ffn_plan_cap(int64_t T, int K, int E, bool has_shared);
 

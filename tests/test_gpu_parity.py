@@ -563,6 +563,22 @@ def test_mlp_split_k(T):
     assert torch.equal(run_mlp(p, x, d, inter), first)
 
 
+@pytest.mark.parametrize("T", [37, 100, 129])
+def test_mlp_stream_k(T):
+    # inter 18432 (144 h blocks) over d = 3584 (28 K blocks): 144 or 288 items do not fill
+    # rounds of 256 workgroups, so the up-projection runs stream-K (runs of 16 or 32 K
+    # blocks that cross h blocks; one tile at T = 37, two 64-row tiles at T = 100, 128-row
+    # tiles with a one-row tail at T = 129)
+    d, inter = 3584, 18432
+    _say(f"moe_mlp stream K d={d} inter={inter} T={T}")
+    p = synth.mlp_weights(d, inter, DEV, seed=11)
+    x = synth.make_x(synth.Dims(d, 1, 1, 1, 1, inter), T, DEV, seed=110 + T)
+    first = run_mlp(p, x, d, inter)
+    assert_rows_close(f64(first), _mlp_ref(_np_params(p), f64(x)), f"mlp stream K T={T}")
+    # each (tile, h block) sums its runs' partial planes in a fixed order
+    assert torch.equal(run_mlp(p, x, d, inter), first)
+
+
 @pytest.mark.slow
 @pytest.mark.parametrize("T", [64, 1000])
 def test_mlp_full_width_sampled_rows(T):
