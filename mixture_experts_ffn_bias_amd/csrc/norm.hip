@@ -31,8 +31,12 @@ __device__ __forceinline__ uint16_t f64_to_bf16(double v) {
 }
 
 constexpr int NORM_THREADS = 256;
-constexpr int NORM_CHUNKS = 8;  // 8-element chunks per thread: d <= 256 * 8 * 8 = 16384
 
+// NCH 8-element chunks per thread (d <= 256 * 8 * NCH).  Every load of the
+// row is issued first, so that a thread's loads are in flight together; a
+// chunk index past the row's end reads the row's last chunk instead and is
+// not used.
+template <int NCH>
 __global__ __launch_bounds__(NORM_THREADS) void add_rmsnorm_kernel(const uint16_t* x,
                                                                     uint16_t* __restrict__ res,
                                                                     const float* __restrict__ gain, float eps,
@@ -40,16 +44,20 @@ __global__ __launch_bounds__(NORM_THREADS) void add_rmsnorm_kernel(const uint16_
   __shared__ double s_part[NORM_THREADS / 64];
   const size_t t = blockIdx.x;
   const int nch = d / 8;
-  uint32_t xw[NORM_CHUNKS][4], rw[NORM_CHUNKS][4];  // the raw bf16 pairs of x and the residual
+  uint32_t xw[NCH][4], rw[NCH][4];  // the raw bf16 pairs of x and the residual
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = min((int)threadIdx.x + NORM_THREADS * i, nch - 1);
+    const uint4 xv = *(const uint4*)(x + t * d + c * 8);
+    const uint4 rv = *(const uint4*)(res + t * d + c * 8);
+    xw[i][0] = xv.x; xw[i][1] = xv.y; xw[i][2] = xv.z; xw[i][3] = xv.w;
+    rw[i][0] = rv.x; rw[i][1] = rv.y; rw[i][2] = rv.z; rw[i][3] = rv.w;
+  }
   double ss = 0.0;
 #pragma unroll
-  for (int i = 0; i < NORM_CHUNKS; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + NORM_THREADS * i;
     if (c < nch) {
-      const uint4 xv = *(const uint4*)(x + t * d + c * 8);
-      const uint4 rv = *(const uint4*)(res + t * d + c * 8);
-      xw[i][0] = xv.x; xw[i][1] = xv.y; xw[i][2] = xv.z; xw[i][3] = xv.w;
-      rw[i][0] = rv.x; rw[i][1] = rv.y; rw[i][2] = rv.z; rw[i][3] = rv.w;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         // the sum of two bf16 values is exact in fp64
@@ -68,7 +76,7 @@ __global__ __launch_bounds__(NORM_THREADS) void add_rmsnorm_kernel(const uint16_
   for (int i = 0; i < NORM_THREADS / 64; ++i) tot += s_part[i];
   const double rs = 1.0 / sqrt(tot / (double)d + (double)eps);
 #pragma unroll
-  for (int i = 0; i < NORM_CHUNKS; ++i) {
+  for (int i = 0; i < NCH; ++i) {
     const int c = threadIdx.x + NORM_THREADS * i;
     if (c < nch) {
       const float4 g0 = *(const float4*)(gain + c * 8);
@@ -95,8 +103,18 @@ __global__ __launch_bounds__(NORM_THREADS) void add_rmsnorm_kernel(const uint16_
 
 hipError_t launch_add_rmsnorm(const uint16_t* x, uint16_t* residual, const float* gain, float eps, int d,
                               int64_t T, uint16_t* out, hipStream_t s) {
-  hipLaunchKernelGGL(add_rmsnorm_kernel, dim3((unsigned)T), dim3(NORM_THREADS), 0, s, x, residual, gain, eps, d,
-                     out);
+  const int per = (d / 8 + NORM_THREADS - 1) / NORM_THREADS;  // chunks per thread (d <= 16384: at most 8)
+  const dim3 g((unsigned)T), b(NORM_THREADS);
+  if (per <= 1)
+    hipLaunchKernelGGL(add_rmsnorm_kernel<1>, g, b, 0, s, x, residual, gain, eps, d, out);
+  else if (per <= 2)
+    hipLaunchKernelGGL(add_rmsnorm_kernel<2>, g, b, 0, s, x, residual, gain, eps, d, out);
+  else if (per <= 4)
+    hipLaunchKernelGGL(add_rmsnorm_kernel<4>, g, b, 0, s, x, residual, gain, eps, d, out);
+  else if (per <= 8)
+    hipLaunchKernelGGL(add_rmsnorm_kernel<8>, g, b, 0, s, x, residual, gain, eps, d, out);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
