@@ -1,15 +1,18 @@
 """Benchmark of the DeepSeek-V3.2-Exp MoE layer forward on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload decode|prefill|skewed|stack4|tiny]
-                    [--weights e4m3|bf16] [--ep-share N] [--fused] [--mlp INTER] [--no-cpu-baseline]
+                    [--extra prefill,skewed,stack4|none] [--tokens T] [--weights e4m3|bf16]
+                    [--ep-share N] [--fused] [--mlp INTER] [--no-cpu-baseline]
 
 A step is one pass of the whole layer (router, permutation, grouped expert
 FFN, combine; for the stacked workload four blocks of fused residual-add
 RMSNorm + layer) over one batch of synthetic, seeded inputs that are resident
-in HBM before timing starts.  Prints one JSON line with tokens/s, the
-roofline position of the dominant kernel (timed with HIP events on the
-library's stream inside the timed region) and the CPU oracle's throughput on a
-bounded sample of the same workload.
+in HBM before timing starts.  Prints one JSON line: the headline workload's
+tokens/s, the roofline position of its dominant kernel (timed with HIP events
+on the library's stream inside the timed region) and the CPU oracle's
+throughput on a sample of the same workload (with the parity of the timed
+GPU output against that oracle call), plus one record per extra workload
+(the compute-bound ones by default) with the same measurements.
 """
 from __future__ import annotations
 
@@ -26,7 +29,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
-BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s (the expert GEMMs run bf16 MFMAs)
+FP8_MFMA_PEAK_TFLOPS = 5000.0   # MI355X dense fp8 matrix peak, TFLOP/s (the figure the metric names)
 STAGES = ("gate", "permute", "ffn_up", "ffn_down", "combine")
 
 
@@ -117,10 +121,17 @@ def measured_traffic(workload: str, kernel: str):
 
 
 def algorithmic_work(dims, T, touched, bf16=False):
-    """Bytes and FLOPs each kernel must move / compute (implementation buffers excluded).
+    """Bytes and FLOPs the method must move / compute, per kernel and per layer.
 
-    touched: number of routed experts with at least one row (the shared expert comes on top).
-    bf16: bf16 expert weights without scales, bf16 activations (x read, h written and read).
+    touched: number of routed experts with at least one row (the shared expert
+    comes on top).  A projection kernel's algorithmic bytes are the weights
+    (and block scales) of the experts it runs, plus, for the up-projection,
+    x read once (its e4m3 codes and scales; bf16 with bf16 weights).  h and
+    the expert output rows o are intermediate buffers of this implementation
+    and are reported apart ("h_bytes", "o_bytes": each written once and read
+    once).  The layer's bytes are every touched expert's weights, the router
+    weight and bias, x in and the update out (bf16).
+    bf16: bf16 expert weights without scales and bf16 activations.
     """
     d, I, K = dims.d_model, dims.inter, dims.topk
     R = T * K + T                                  # routed rows + shared rows
@@ -132,14 +143,31 @@ def algorithmic_work(dims, T, touched, bf16=False):
         up_w = 2 * I * d + 2 * (I // 128) * (d // 128) * 4
         dn_w = I * d + (d // 128) * (I // 128) * 4
         x_bytes, h_bytes = T * d + T * (d // 128) * 4, R * (I + (I // 128) * 4)
-    up_bytes = ne * up_w + x_bytes + h_bytes
-    dn_bytes = ne * dn_w + h_bytes + R * d * 2
     return {
-        "ffn_up": {"bytes": up_bytes, "flops": 2 * R * d * 2 * I},
-        "ffn_down": {"bytes": dn_bytes, "flops": 2 * R * I * d},
+        "ffn_up": {"bytes": ne * up_w + x_bytes, "flops": 2 * R * d * 2 * I},
+        "ffn_down": {"bytes": ne * dn_w, "flops": 2 * R * I * d},
+        "h_bytes": h_bytes,
+        "o_bytes": R * d * 2,
         "layer_bytes": ne * (up_w + dn_w) + dims.n_experts * d * 4 + dims.n_experts * 4 + 2 * T * d * 2,
         "layer_flops": 2 * R * 3 * d * I,
     }
+
+
+def roofline_position(alg_bytes, alg_flops, seconds):
+    """Achieved HBM rate and matrix rate of a kernel or step, each as a fraction of
+    its MI355X peak (bf16 MFMA, which the expert GEMMs use, and the fp8 figure),
+    and which of HBM and bf16 MFMA binds (the larger fraction)."""
+    gbs = alg_bytes / seconds / 1e9
+    tfs = alg_flops / seconds / 1e12
+    hbm, bf16, fp8 = gbs / HBM_PEAK_GBS, tfs / BF16_MFMA_PEAK_TFLOPS, tfs / FP8_MFMA_PEAK_TFLOPS
+    if hbm >= bf16:
+        head = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(hbm, 4)}
+    else:
+        head = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(bf16, 4)}
+    head.update({"hbm_GBps": round(gbs, 1), "hbm_frac": round(hbm, 4), "TFLOPs": round(tfs, 1),
+                 "bf16_mfma_frac": round(bf16, 4), "fp8_mfma_frac": round(fp8, 4)})
+    return head
 
 
 def _host(t):
@@ -150,14 +178,27 @@ def _host(t):
     return t.view(torch.int16).numpy().view(np.uint16) if t.dtype == torch.bfloat16 else t.numpy()
 
 
-def cpu_baseline(x, params, dims, budget_s, threads, residual=None, gain=None, seed=0):
-    """The oracle on host cores over a bounded, seeded sample of tokens.
+def host_threads() -> int:
+    """Host threads for the oracle: the process's CPU share (OMP_NUM_THREADS when set), at most the cores."""
+    n = os.cpu_count() or 1
+    try:
+        return max(1, min(n, int(os.environ.get("OMP_NUM_THREADS", n))))
+    except ValueError:
+        return n
 
-    Tokens are taken two at a time in a seeded random order until budget_s
-    seconds of oracle work have been spent.  The weights of the experts a
-    batch needs are copied to host memory before its timed call.  With a
-    residual and gain, each timed call also includes the fused residual-add
-    RMSNorm in front of the layer.
+
+def cpu_baseline(x, params, dims, threads, tokens, residual=None, gain=None, gpu_delta=None, gpu_idx=None):
+    """The oracle on host cores: ONE call over the token sample `tokens`.
+
+    The weights of the experts the sample selects are copied to host memory
+    before the timed call; the call itself runs the router, dequantises each
+    of those experts once, evaluates them and the shared expert in float64
+    and combines.  With a residual and gain, the fused residual-add RMSNorm in
+    front of the layer is in the timed call too.  When the GPU's output and
+    routing of the same layer are given, the parity of the GPU output on the
+    sample against this call's result comes back as well (tokens whose oracle
+    selection margin is below 1e-5 and that the GPU routes differently are
+    left out of the output figures and counted).
     """
     import numpy as np
     import torch
@@ -166,114 +207,79 @@ def cpu_baseline(x, params, dims, budget_s, threads, residual=None, gain=None, s
     import oracle
 
     torch.set_num_threads(threads)
-    rng = np.random.default_rng(seed)
-    T = x.shape[0]
-    order = rng.permutation(T)
+    tok = np.asarray(tokens, dtype=np.int64)
     names = ("w1", "s1", "w3", "s3", "w2", "s2") if "s1" in params else ("w1", "w3", "w2")
-    xv_all = x.float().cpu().numpy().astype(np.float64)
-    rv_all = residual.float().cpu().numpy().astype(np.float64) if residual is not None else None
+    xv = x[torch.from_numpy(tok).to(x.device)].float().cpu().numpy().astype(np.float64)
+    rv = residual[torch.from_numpy(tok).to(x.device)].float().cpu().numpy().astype(np.float64) \
+        if residual is not None else None
     gv = gain.cpu().numpy() if gain is not None else None
     host = {"gate_w": params["gate_w"].cpu().numpy(), "gate_b": params["gate_b"].cpu().numpy()}
     for n in names:
         host["sh_" + n] = _host(params["sh_" + n])
-    cache = {}
-
-    class Rows:
-        def __init__(self, n):
-            self.n = n
-
-        def __getitem__(self, e):
-            if (self.n, e) not in cache:           # only reached if a batch needs an unfetched expert
-                cache[(self.n, e)] = _host(params[self.n][e])
-            return cache[(self.n, e)]
-
-    for n in names:
-        host[n] = Rows(n)
-    done, elapsed, i = 0, 0.0, 0
     with threadpool_limits(limits=threads):
-        while i < T and elapsed < budget_s:
-            batch = order[i:i + 2]
-            i += len(batch)
-            xb = xv_all[batch]
-            if rv_all is not None:
-                xin, _ = oracle.add_rmsnorm(xb, rv_all[batch], gv)
-            else:
-                xin = xb
-            sel = oracle.gate(xin, host["gate_w"], host["gate_b"], dims)["idx"]
-            if len(cache) > 6 * 300:
-                cache.clear()
-            for e in set(sel.ravel().tolist()):     # untimed: host copies of the needed weights
-                for n in names:
-                    host[n][e]
-            t0 = time.perf_counter()
-            if rv_all is not None:
-                xin, _ = oracle.add_rmsnorm(xb, rv_all[batch], gv)
-            oracle.moe_forward(xin, host, dims)
-            elapsed += time.perf_counter() - t0
-            done += len(batch)
+        xin = oracle.add_rmsnorm(xv, rv, gv)[0] if rv is not None else xv
+        sel = oracle.gate(xin, host["gate_w"], host["gate_b"], dims)["idx"]
+        need = sorted(set(sel.ravel().tolist()))
+        for n in names:                            # untimed: host copies of the selected experts' weights
+            full = params[n]
+            host[n] = {e: _host(full[e]) for e in need}
+        t0 = time.perf_counter()
+        if rv is not None:
+            xin = oracle.add_rmsnorm(xv, rv, gv)[0]
+        ref = oracle.moe_forward(xin, host, dims)
+        elapsed = time.perf_counter() - t0
     what = "fused residual-add RMSNorm + layer" if residual is not None else "layer"
-    return {"value": round(done / elapsed, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} of {T} tokens (seeded random order, 2 per call), {what}: router + the experts "
-                      f"the sample selects + shared expert, float64, {elapsed:.1f} s of oracle time"}
+    base = {"value": round(tok.size / elapsed, 3), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{tok.size} of {x.shape[0]} tokens in one oracle call ({what}: router, the {len(need)} "
+                      f"experts the sample selects, each dequantised once, and the shared expert, float64), "
+                      f"{elapsed:.1f} s on {threads} host threads"}
+    parity = None
+    if gpu_delta is not None and gpu_idx is not None:
+        r = ref["routing"]
+        gi = np.sort(gpu_idx[tok], axis=1)
+        same = np.all(gi == np.sort(r["idx"], axis=1), axis=1)
+        near = (r["expert_gap"] < 1e-5) | (r["group_gap"] < 1e-5)
+        got = gpu_delta[torch.from_numpy(tok).to(gpu_delta.device)].float().cpu().numpy().astype(np.float64)
+        y = ref["y"]
+        diff = np.abs(got[same] - y[same])
+        parity = {"tokens": int(tok.size), "routing_identical": int(same.sum()),
+                  "routed_differently_near_tie": int((~same & near).sum()),
+                  "routed_differently_not_near_tie": int((~same & ~near).sum()),
+                  "near_tie_tokens": int(near.sum()),
+                  "max_abs_over_rms": float(diff.max() / np.sqrt(np.mean(y[same] ** 2))),
+                  "mean_rel": float(diff.mean() / np.abs(y[same]).mean()),
+                  "bounds": {"max_abs_over_rms": 2e-2, "mean_rel": 5e-3}}
+    return base, parity
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skewed", "stack4"])
-    ap.add_argument("--weights", default="e4m3", choices=["e4m3", "bf16"],
-                    help="expert weights: FP8 e4m3 with 128x128 block scales (the layer's), or bf16 without scales")
-    ap.add_argument("--ep-share", type=int, default=0, metavar="N",
-                    help="time one rank's share of an N-way expert-parallel layer instead: experts [0, E/N) "
-                         "plus the shared expert over all tokens (moe_forward_shard, fp32 partial output)")
-    ap.add_argument("--fused", action="store_true",
-                    help="time the single-launch forward (moe_forward_fused: one kernel for the whole layer, "
-                         "at most 64 tokens, e4m3 weights) instead of the per-step kernels")
-    ap.add_argument("--mlp", type=int, default=0, metavar="INTER",
-                    help="time the dense SwiGLU MLP of the blocks before the MoE blocks instead (moe_mlp, FP8 "
-                         "weights d_model -> INTER -> d_model, e.g. 18432) over the workload's tokens")
-    ap.add_argument("--tokens", type=int, default=0,
-                    help="with --mlp: the batch's token count (default: the workload's)")
-    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle work for cpu_baseline")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: the layer runs on a single GPU here, and a rank's expert "
-              "share on one GPU is timed with --ep-share N (run with --gpus 1).", file=sys.stderr)
-        sys.exit(2)
+def gpu_info(torch):
+    """Device name and clocks (best effort: rocm-smi's current clocks when it answers)."""
+    import subprocess
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "hbm_GiB": round(p.total_memory / 2 ** 30, 1)}
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
+        clk = {}
+        for m in re.finditer(r"(sclk|mclk|fclk|socclk) clock level: \d+: \((\d+)Mhz\)", out):
+            clk.setdefault(m.group(1) + "_MHz", int(m.group(2)))
+        info["clocks"] = clk or None
+    except (OSError, subprocess.SubprocessError):
+        info["clocks"] = None
+    return info
 
-    import numpy as np
-    import torch
 
-    import mixture_experts_ffn_bias_amd as moe
-    import synth
+def bench_layer(name, args, moe, synth, torch, np, dev, tokens=0):
+    """Warm-up, then `args.steps` timed steps of workload `name`.
 
-    dev = "cuda:0"
-    torch.cuda.set_device(0)
-    if args.copy_calibration:
-        n = 1 << 30
-        src = torch.ones(n, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration_bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 3}))
-        return
-    if args.ep_share:
-        return bench_share(args, moe, synth, torch, np, dev)
-    if args.fused:
-        return bench_fused(args, moe, synth, torch, np, dev)
-    if args.mlp:
-        return bench_mlp(args, moe, synth, torch, np, dev)
-    wl = synth.WORKLOADS[args.workload]
+    Returns (record, ctx): the record holds the step time, tokens/s, the touched
+    experts, each stage's time (HIP events on the library's stream) and the
+    roofline position of the dominant kernel; ctx holds the data the CPU
+    baseline needs (freed by the caller)."""
+    wl = synth.WORKLOADS[name]
     dims = wl.dims
     bf16 = args.weights == "bf16"
-    data = synth.make_workload(args.workload, device=dev, weights=args.weights)
+    data = synth.make_workload(name, device=dev, weights=args.weights, tokens=tokens or None)
     T = data["tokens"]
     cd = moe.make_dims(dims.d_model, dims.n_experts, dims.n_groups, dims.topk_groups, dims.topk, dims.inter,
                        dims.route_scale)
@@ -324,8 +330,7 @@ def main():
     for k in range(K):
         step(evs[k])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
+    wall = time.perf_counter() - t0
 
     stage_ms = {s: 0.0 for s in STAGES}
     for k in range(K):
@@ -337,60 +342,139 @@ def main():
     stage_avg = {s: v / launches for s, v in stage_ms.items()}
     hev.close()
 
-    # algorithmic work of the dominant kernel (per launch; blocks of the stack are alike)
     counts = [np.bincount(i.cpu().numpy().ravel(), minlength=dims.n_experts) for i in idx]
     touched = [int((c > 0).sum()) for c in counts]
     work = [algorithmic_work(dims, T, t, bf16) for t in touched]
     dom = max(("ffn_up", "ffn_down"), key=lambda s: stage_avg[s])
-    dur = stage_avg[dom] * 1e-3
-    bytes_per = sum(wk[dom]["bytes"] for wk in work) / nb
+    bytes_per = sum(wk[dom]["bytes"] for wk in work) / nb      # per launch (the blocks of the stack are alike)
     flops_per = sum(wk[dom]["flops"] for wk in work) / nb
-    gbs = bytes_per / dur / 1e9
-    tfs = flops_per / dur / 1e12
-    if gbs / HBM_PEAK_GBS >= tfs / BF16_MFMA_PEAK_TFLOPS:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4)}
-    traffic_key = args.workload + ("_bf16" if bf16 else "")
+    roof = roofline_position(bytes_per, flops_per, stage_avg[dom] * 1e-3)
+    traffic_key = name + ("_bf16" if bf16 else "")
     roof.update({"kernel": dom, "traffic": measured_traffic(traffic_key, dom), "launch_ms": round(stage_avg[dom], 4),
-                 "alg_bytes": int(bytes_per), "alg_flops": int(flops_per)})
-
-    tokens = T * K
-    layer_bytes = sum(wk["layer_bytes"] for wk in work)
+                 "alg_bytes": int(bytes_per), "alg_flops": int(flops_per),
+                 "h_bytes": int(sum(wk["h_bytes"] for wk in work) / nb),
+                 "o_bytes": int(sum(wk["o_bytes"] for wk in work) / nb)})
     step_s = wall / K
+    layer_bytes = sum(wk["layer_bytes"] for wk in work)
+    layer_flops = sum(wk["layer_flops"] for wk in work)
+    layer = roofline_position(layer_bytes, layer_flops, step_s)
+    layer.update({"alg_bytes_per_step": int(layer_bytes), "alg_flops_per_step": int(layer_flops),
+                  "stage_ms": {s: round(v, 4) for s, v in stage_avg.items()}})
+    rec = {"workload": name, "tokens": T, "blocks": nb, "steps": K, "ms_per_step": round(step_s * 1e3, 4),
+           "tokens_per_s": round(T * K / wall, 2), "touched_experts": touched, "roofline": roof, "layer": layer}
+    ctx = {"data": data, "dims": dims, "delta": delta, "idx": idx, "layers": layers, "ws": ws}
+    return rec, ctx
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["tiny", "decode", "prefill", "skewed", "stack4"],
+                    help="the headline workload (its figures are the line's value and roofline)")
+    ap.add_argument("--extra", default="prefill,skewed,stack4",
+                    help="comma-separated workloads timed after the headline and reported under 'workloads' "
+                         "('none' for none)")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="token count of the headline workload (default: the workload's own); with --mlp: "
+                         "the MLP's batch")
+    ap.add_argument("--weights", default="e4m3", choices=["e4m3", "bf16"],
+                    help="expert weights: FP8 e4m3 with 128x128 block scales (the layer's), or bf16 without scales")
+    ap.add_argument("--ep-share", type=int, default=0, metavar="N",
+                    help="time one rank's share of an N-way expert-parallel layer instead: experts [0, E/N) "
+                         "plus the shared expert over all tokens (moe_forward_shard, fp32 partial output)")
+    ap.add_argument("--fused", action="store_true",
+                    help="time the single-launch forward (moe_forward_fused: one kernel for the whole layer, "
+                         "at most 64 tokens, e4m3 weights) instead of the per-step kernels")
+    ap.add_argument("--mlp", type=int, default=0, metavar="INTER",
+                    help="time the dense SwiGLU MLP of the blocks before the MoE blocks instead (moe_mlp, FP8 "
+                         "weights d_model -> INTER -> d_model, e.g. 18432) over the workload's tokens")
+    ap.add_argument("--cpu-tokens", type=int, default=64,
+                    help="tokens in the CPU baseline's one oracle call (the whole batch when it is smaller)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the layer runs on a single GPU here, and a rank's expert "
+              "share on one GPU is timed with --ep-share N (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import mixture_experts_ffn_bias_amd as moe
+    import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 3}))
+        return
+    if args.ep_share:
+        return bench_share(args, moe, synth, torch, np, dev)
+    if args.fused:
+        return bench_fused(args, moe, synth, torch, np, dev)
+    if args.mlp:
+        return bench_mlp(args, moe, synth, torch, np, dev)
+    bf16 = args.weights == "bf16"
+    rec, ctx = bench_layer(args.workload, args, moe, synth, torch, np, dev, tokens=args.tokens)
+    dims = ctx["dims"]
     out = {
         "metric": "MoE layer tokens/s (d7168,256e,top8) + % of fp8 MFMA / HBM roofline",
-        "value": round(tokens / wall, 2),
+        "value": rec["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(step_s * 1e3, 4),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": T, "blocks": nb, "d_model": dims.d_model,
-                   "experts": dims.n_experts, "groups": dims.n_groups, "topk_groups": dims.topk_groups,
-                   "topk": dims.topk, "inter": dims.inter,
+        "config": {"workload": args.workload, "tokens": rec["tokens"], "blocks": rec["blocks"],
+                   "d_model": dims.d_model, "experts": dims.n_experts, "groups": dims.n_groups,
+                   "topk_groups": dims.topk_groups, "topk": dims.topk, "inter": dims.inter,
                    "weights": "bf16, no scales" if bf16 else "e4m3 + fp32 128x128 block scales",
-                   "touched_experts": touched},
-        "roofline": roof,
-        "layer": {"alg_bytes_per_step": int(layer_bytes), "hbm_GBps": round(layer_bytes / step_s / 1e9, 1),
-                  "hbm_frac": round(layer_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
-                  "stage_ms": {s: round(v, 4) for s, v in stage_avg.items()}},
+                   "touched_experts": rec["touched_experts"]},
+        "roofline": rec["roofline"],
+        "layer": rec["layer"],
+        "gpu": gpu_info(torch),
     }
     if not args.no_cpu_baseline:
-        threads = max(1, min(16, os.cpu_count() or 1))
-        if nb > 1:
-            out["cpu_baseline"] = cpu_baseline(x0, data["blocks"][0], dims, args.cpu_budget, threads,
-                                               residual=data["residual"], gain=data["gains"][0])
-            out["cpu_baseline"]["sample"] += "; first block of the stack, so tokens/s per block"
+        data, T = ctx["data"], rec["tokens"]
+        n = min(T, args.cpu_tokens)
+        tok = np.sort(np.random.default_rng(0).choice(T, n, replace=False)) if n < T else np.arange(T)
+        threads = host_threads()
+        if rec["blocks"] > 1:
+            base, parity = cpu_baseline(data["x"], data["blocks"][0], dims, threads, tok,
+                                        residual=data["residual"], gain=data["gains"][0])
+            base["sample"] += "; the first block of the stack, so tokens/s per block"
         else:
-            out["cpu_baseline"] = cpu_baseline(x0, data["blocks"][0], dims, args.cpu_budget, threads)
+            base, parity = cpu_baseline(data["x"], data["blocks"][0], dims, threads, tok, gpu_delta=ctx["delta"],
+                                        gpu_idx=ctx["idx"][0].cpu().numpy())
+        out["cpu_baseline"] = base
+        if parity is not None:
+            out["parity"] = parity
+    del ctx
+    torch.cuda.empty_cache()
+    extra = [] if args.extra in ("", "none") else [w for w in args.extra.split(",") if w != args.workload]
+    if extra:
+        out["workloads"] = {}
+        for name in extra:
+            r, c = bench_layer(name, args, moe, synth, torch, np, dev)
+            del c
+            torch.cuda.empty_cache()
+            out["workloads"][name] = r
     print(json.dumps(out), flush=True)
 
 
@@ -441,14 +525,7 @@ def bench_share(args, moe, synth, torch, np, dev):
     wbytes = (touched + 1) * (3 * I * d + 3 * (I // 128) * (d // 128) * 4)
     alg = wbytes + T * d * 2 + T * dims.topk * 8 + T * d * 4
     flops = 2 * rows * 3 * d * I
-    gbs = alg / (step_ms * 1e-3) / 1e9
-    tfs = flops / (step_ms * 1e-3) / 1e12
-    if gbs / HBM_PEAK_GBS >= tfs / BF16_MFMA_PEAK_TFLOPS:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(gbs / HBM_PEAK_GBS, 4)}
-    else:
-        roof = {"bound": "mfma", "achieved": round(tfs, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tfs / BF16_MFMA_PEAK_TFLOPS, 4)}
+    roof = roofline_position(alg, flops, step_ms * 1e-3)
     roof.update({"kernel": "share step (permute + FFN + partial combine)", "traffic": None,
                  "launch_ms": round(step_ms, 4), "alg_bytes": int(alg), "alg_flops": int(flops)})
     out = {
@@ -469,7 +546,7 @@ def bench_fused(args, moe, synth, torch, np, dev):
     dims = wl.dims
     if wl.blocks != 1 or args.weights != "e4m3":
         sys.exit("--fused takes a single-block workload and e4m3 weights")
-    data = synth.make_workload(args.workload, device=dev)
+    data = synth.make_workload(args.workload, device=dev, tokens=args.tokens or None)
     T = data["tokens"]
     if T > moe.FUSED_MAX_TOKENS:
         sys.exit(f"--fused runs at most {moe.FUSED_MAX_TOKENS} tokens (workload has {T})")
@@ -552,14 +629,7 @@ def bench_mlp(args, moe, synth, torch, np, dev):
     wbytes = 3 * d * inter + 3 * (d // 128) * (inter // 128) * 4
     alg_bytes = wbytes + 2 * T * d * 2                      # weights once, x in, out
     alg_flops = 6 * T * d * inter
-    if alg_flops / alg_bytes > BF16_MFMA_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9):
-        ach = alg_flops / (launch_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4)}
-    else:
-        ach = alg_bytes / (launch_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4)}
+    roof = roofline_position(alg_bytes, alg_flops, launch_ms * 1e-3)
     roof.update({"kernel": "dense MLP (quantisation + up- and down-projection)", "traffic": None,
                  "launch_ms": round(launch_ms, 4), "alg_bytes": int(alg_bytes), "alg_flops": int(alg_flops)})
     res = {

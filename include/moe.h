@@ -186,9 +186,18 @@ int moe_combine(const moe_dims* dims, int64_t tokens, const int32_t* idx, const 
                 const int32_t* pair_row, const uint16_t* rows, int32_t has_shared,
                 uint16_t* delta, void* stream);
 
-/* The whole layer: gate -> permute -> grouped FFN -> combine, with no host
- * synchronisation.  x bf16 [T][d] -> delta bf16 [T][d].  idx_out / w_out
- * (int32 / fp32 [T][K]) receive the routing when non-NULL. */
+/* The whole layer ("DeepSeek-V3.2-Exp · MoE update": the moe-forward excerpt
+ * flattens x to [tokens, d], calls the gate, counts the tokens per expert,
+ * runs each selected expert on its tokens and adds the router-weighted
+ * outputs into an fp32 accumulator in ascending expert id, adds the shared
+ * expert's output for every token, and casts the sum back to x's dtype, the
+ * page's output expression and shape; "Add shared output", formula):
+ * gate -> permute -> grouped FFN -> combine, enqueued with no host
+ * synchronisation (the per-expert counts stay on the device).
+ *   x       bf16 [T][d] (16-byte aligned)
+ *   delta   bf16 [T][d] out, the layer's update (16-byte aligned; must not alias x)
+ *   idx_out int32 [T][K], w_out fp32 [T][K]: out, the routing, when non-NULL
+ * Needs moe_workspace_size(dims, T) bytes of workspace (256-byte aligned). */
 int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens,
                 const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
                 void* workspace, size_t workspace_bytes, void* stream);

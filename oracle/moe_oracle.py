@@ -45,9 +45,14 @@ same rule the weights use), the block products are summed exactly, and the
 Linear output is rounded to bfloat16 (it returns the activation dtype, which
 is why the expert converts it to float32 before SiLU).
 
-Every floating-point step is evaluated in float64 (exact for all e4m3 x e4m3
-block sums); the roundings the pages place (bf16 Linear outputs, bf16 h,
-float32 scale arithmetic of the quantiser) are applied explicitly.
+Every floating-point step is evaluated in float64.  The Linear layers multiply
+the dequantised operands (e4m3 value times its float32 scale, exact in
+float64) with BLAS matrix products: each product of two dequantised values
+has up to 56 significant bits and is rounded to float64's 53, and the
+summation order is BLAS's own, so a Linear output carries a relative error
+of about 1e-16 before it is rounded to bfloat16.  The roundings the pages
+place (bf16 Linear outputs, bf16 h, float32 scale arithmetic of the
+quantiser) are applied explicitly.
 """
 from __future__ import annotations
 
@@ -66,7 +71,7 @@ __all__ = [
     "BLOCK", "E4M3_MAX", "RMS_EPS",
     "e4m3_table", "e4m3_decode", "e4m3_encode", "bf16_round", "bf16_bits_to_f64",
     "f64_to_bf16_bits", "dequant_weight", "quant_act", "dequant_act", "gate", "permute",
-    "silu", "expert_ffn", "expert_ffn_bf16", "bf16_weight", "moe_forward", "add_rmsnorm", "param_count",
+    "silu", "expert_ffn", "expert_ffn_bf16", "bf16_weight", "combine", "moe_forward", "add_rmsnorm", "param_count",
     "weights_for",
 ]
 
@@ -345,6 +350,29 @@ def bf16_weight(w) -> np.ndarray:
 # "Add shared output" formula)
 # --------------------------------------------------------------------------
 
+def combine(idx, w, outs, shared) -> np.ndarray:
+    """Router-weighted sum of a token's expert outputs plus the shared output.
+
+    idx [n, K] selected experts, w [n, K] router weights, outs [n, K, d] the
+    output of expert idx[t, k] on token t, shared [n, d] the shared expert's
+    output.  y[t] = sum over the K choices, taken in ascending expert id, of
+    w[t, k] * outs[t, k], then + shared[t] ("MoE update", moe-forward excerpt:
+    experts are visited in ascending id into a float32 accumulator and the
+    shared expert's output comes last; here float64).
+    """
+    idx = np.asarray(idx, dtype=np.int64)
+    w = np.asarray(w, dtype=np.float64)
+    outs = np.asarray(outs, dtype=np.float64)
+    n, K = idx.shape
+    y = np.zeros((n, outs.shape[-1]), dtype=np.float64)
+    order = np.argsort(idx, axis=1, kind="stable")          # each token's choices by ascending expert id
+    at = np.arange(n)
+    for j in range(K):
+        k = order[:, j]
+        y += w[at, k][:, None] * outs[at, k]
+    return y + np.asarray(shared, dtype=np.float64)
+
+
 def moe_forward(x, params, dims, tokens: Optional[Sequence[int]] = None,
                 idx: Optional[np.ndarray] = None, routing: Optional[Dict] = None) -> Dict[str, np.ndarray]:
     """Forward of one MoE layer on bf16 x [T, d] (given as float64 values).
@@ -357,6 +385,14 @@ def moe_forward(x, params, dims, tokens: Optional[Sequence[int]] = None,
     from the oracle's own scores).  routing: a gate() result to reuse.
     Returns routing, y (float64, unrounded) and delta = bf16(y) for the
     evaluated tokens.
+
+    The update of token t is the sum over its K choices, taken in ascending
+    expert id, of the router weight times the expert's output on x[t], plus
+    the shared expert's output on x[t] ("MoE update", moe-forward excerpt:
+    experts are visited in ascending id and the shared expert comes last;
+    "Add shared output", formula).  The expert outputs are evaluated one
+    expert at a time over all rows that chose it, so each expert's weights
+    are dequantised once.
     """
     x = np.asarray(x, dtype=np.float64)
     T, d = x.shape
@@ -364,17 +400,14 @@ def moe_forward(x, params, dims, tokens: Optional[Sequence[int]] = None,
     sel_idx = r["idx"] if idx is None else np.asarray(idx, dtype=np.int64)
     w_all = r["w"] if idx is None else weights_for(r["s"], sel_idx, dims.route_scale)
     tok = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    n, K = tok.size, sel_idx.shape[1]
 
-    y = np.zeros((tok.size, d), dtype=np.float64)
-    ti = sel_idx[tok]
-    tw = w_all[tok]
-    for e in range(dims.n_experts):                 # ascending expert id
-        rows, ks = np.nonzero(ti == e)             # ascending token
-        if rows.size == 0:
-            continue
-        o = _run_expert(params, e, x[tok[rows]])
-        y[rows] += o * tw[rows, ks][:, None]
-    y += _run_expert(params, None, x[tok])  # shared expert, every token
+    choice = sel_idx[tok]                                   # [n, K] expert of each choice
+    outs = np.zeros((n, K, d), dtype=np.float64)            # expert output of each (token, choice)
+    for e in np.unique(choice):
+        tt, kk = np.nonzero(choice == e)
+        outs[tt, kk] = _run_expert(params, int(e), x[tok[tt]])
+    y = combine(choice, w_all[tok], outs, _run_expert(params, None, x[tok]))
     return {"idx": sel_idx, "w": w_all, "routing": r, "tokens": tok, "y": y, "delta": bf16_round(y)}
 
 

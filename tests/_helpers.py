@@ -14,6 +14,7 @@ import numpy as np
 import torch
 
 import mixture_experts_ffn_bias_amd as moe
+import oracle
 
 NEAR_TIE = 1e-5
 MAX_REL = 2e-2
@@ -119,3 +120,48 @@ def assert_rows_close(gpu: np.ndarray, ref: np.ndarray, what: str, within_ulp: f
     _, mean = metrics(gpu, ref)
     print(f"[parity] {what}: within 1 ulp {frac:.5f}, mean rel={mean:.3e}", flush=True)
     assert frac >= within_ulp and mean <= MEAN_REL, f"{what}: within-ulp {frac:.4f}, mean {mean:.3e}"
+
+
+def tile_rows(T: int, bf16: bool = False) -> int:
+    """Rows per FFN tile of the routed layer for a batch of T tokens (the
+    library's choice): 32 up to 128 tokens, then 128 (e4m3 and bf16 expert
+    weights alike)."""
+    return 32 if T <= 128 else 128
+
+
+def tile_starts(count: int, T: int, bf16: bool = False):
+    """First rows (relative to the expert's first row) of the FFN tiles after
+    the first, for an expert with `count` permuted rows in a batch of T tokens:
+    an expert with more rows than one tile holds is cut into ceil(count / rows)
+    tiles of equal size, rounded up to 16 rows (the library's tile plan)."""
+    nt_rows = tile_rows(T, bf16)
+    n = -(-count // nt_rows)
+    if n <= 1:
+        return []
+    rt = min(nt_rows, -(-(-(-count // n)) // 16) * 16)
+    return [j * rt for j in range(1, n)]
+
+
+def sample_tokens(idx: np.ndarray, n_experts: int, T: int, at_least: int, seed: int,
+                  bf16: bool = False) -> np.ndarray:
+    """First and last permuted row of every touched expert, both sides of every
+    tile boundary of multi-tile experts and of the shared expert, plus seeded
+    random tokens up to `at_least`."""
+    perm = oracle.permute(idx, n_experts)
+    off, rt = perm["offsets"], perm["row_token"]
+    pick = set()
+    for e in range(n_experts):
+        lo, hi = int(off[e]), int(off[e + 1])
+        if hi == lo:
+            continue
+        pick.update((int(rt[lo]), int(rt[hi - 1])))
+        for b in tile_starts(hi - lo, T, bf16):
+            pick.update((int(rt[lo + b - 1]), int(rt[lo + b])))
+    nt_rows = tile_rows(T, bf16)
+    for j in range(1, -(-T // nt_rows)):          # the shared expert's tiles: rows in token order
+        pick.update((j * nt_rows - 1, j * nt_rows))
+    rng = np.random.default_rng(seed)
+    rest = np.setdiff1d(np.arange(T), np.fromiter(pick, dtype=np.int64))
+    need = max(0, min(at_least - len(pick), rest.size))
+    pick.update(rng.choice(rest, need, replace=False).tolist())
+    return np.array(sorted(pick), dtype=np.int64)

@@ -108,6 +108,21 @@ def test_combine_is_weighted_sum_of_selected_experts():
     assert np.allclose(out["y"][t], want, rtol=1e-12, atol=1e-12)
 
 
+def test_combine_adds_choices_in_ascending_expert_id_then_shared():
+    # float64 sums whose value depends on the order: the expert-1 row holds 1e16,
+    # expert 3 holds 1 and expert 5 holds -1e16.  Ascending expert id gives
+    # (1e16 + 1) - 1e16 = 0; the order of the choices as given (5, 1, 3) would give 1
+    idx = np.array([[5, 1, 3], [2, 0, 4]])
+    w = np.array([[1.0, 1.0, 1.0], [0.5, 2.0, 0.25]])
+    outs = np.zeros((2, 3, 2))
+    outs[0, :, 0] = [-1e16, 1e16, 1.0]
+    outs[1] = [[2.0, 4.0], [1.0, 8.0], [16.0, 32.0]]
+    shared = np.array([[10.0, 0.5], [0.0, 0.0]])
+    y = oracle.combine(idx, w, outs, shared)
+    assert y[0, 0] == 10.0 and y[0, 1] == 0.5
+    assert np.array_equal(y[1], [2.0 * 1.0 + 0.5 * 2.0 + 0.25 * 16.0, 2.0 * 8.0 + 0.5 * 4.0 + 0.25 * 32.0])
+
+
 @pytest.mark.parametrize("T,E,K", [(64, 16, 4), (1000, 256, 8), (1, 8, 8), (0, 16, 4)])
 def test_permutation_invariants(T, E, K):
     rng = np.random.default_rng(T + E)
