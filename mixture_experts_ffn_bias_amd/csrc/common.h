@@ -20,6 +20,29 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_floa
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 __device__ __forceinline__ float round_bf16(float f) { return bf16_to_f32(f32_to_bf16(f)); }
 
+// bf16 nearest (ties to even) of a double, rounded once: the conversion to
+// float rounds to odd (inexact results get their last bit set), which keeps
+// the following round-to-nearest-even to bf16 correct.
+__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
+  float f = (float)v;
+  const double back = (double)f;
+  if (back != v) {
+    uint32_t u = __float_as_uint(f);
+    // towards v in magnitude (from a zero f, whose magnitude is below v's,
+    // to the smallest subnormal of v's sign)
+    if ((u & 1u) == 0u) u += fabs(back) < fabs(v) ? 1u : 0xFFFFFFFFu;
+    f = __uint_as_float(u);
+  }
+  return f32_to_bf16(f);
+}
+
+// Whether rounding the fp32 value f to bf16 could go the other way for a
+// value within `ulps` fp32 units in the last place of f: the 16 bits that
+// the rounding drops lie within `ulps` of the halfway pattern 0x8000.
+__device__ __forceinline__ bool near_bf16_tie(float f, uint32_t ulps) {
+  return ((__float_as_uint(f) & 0xFFFFu) - (0x8000u - ulps)) < 2u * ulps + 1u;
+}
+
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 
 // A 128-deep e4m3 block operand, decoded to bfloat16 (exact: every e4m3 value

@@ -428,6 +428,7 @@ struct Item {
   const float* sa0;    // weight block scales of the two weight groups over K (e4m3)
   const float* sa1;
   int blk;             // up: the 128-wide h block; down: the pair of 128-feature output blocks
+  int expert;          // the tile's expert (routed experts first, then the shared one)
   int row0, nrows;     // the tile's permuted rows
   bool once;           // the tile is the only one of its expert
   int nkb;             // K blocks multiplied
@@ -488,6 +489,7 @@ __device__ __forceinline__ void up_item_of(const FfnArgs& a, int4 td, int ib, It
   it.sa0 = BF ? nullptr : P.s1 + (eo * nib + ib) * nkb;
   it.sa1 = BF ? nullptr : P.s3 + (eo * nib + ib) * nkb;
   it.blk = ib;
+  it.expert = e;
   it.row0 = row0;
   it.nrows = nrows;
   it.once = td.w != 0;
@@ -534,6 +536,7 @@ __device__ __forceinline__ void down_item_of(const FfnArgs& a, int4 td, int ob, 
   it.sa0 = BF ? nullptr : P.s2 + (eo * nob + min(2 * ob, nob - 1)) * nkb;
   it.sa1 = BF ? nullptr : P.s2 + (eo * nob + min(2 * ob + 1, nob - 1)) * nkb;
   it.blk = ob;
+  it.expert = e;
   it.row0 = row0;
   it.nrows = nrows;
   it.once = td.w != 0;
@@ -566,10 +569,163 @@ __device__ __forceinline__ int item_mvalid(const Item<ROWS>& it) {
   return __builtin_amdgcn_readfirstlane(min(Tile<ROWS>::MVMAX, max(0, (it.nrows - wr * 64 + 15) >> 4)));
 }
 
+// Rounding g and u as their exact values round.  A Linear output is an fp32
+// sum of d / 128 scaled block products.  Its error is a few units of 2^-24
+// times the size of the partial sums (measured against the exact sums on the
+// CPU: median 0.5, 99.99th percentile 7, largest 12 units of 2^-24 x the
+// largest |sum| of the row among a wave's 32 columns), so when the exact value lies
+// near a bf16 rounding midpoint the fp32 sum may round to the other
+// neighbour.  A sum is "uncertain" when it lies within TIE_ULPS of its own
+// ulps plus TIE_ABS x 2^-24 x that row maximum of a midpoint; the bf16 values
+// that an interval of that width around it rounds to are its candidates.  An
+// uncertain element is recomputed exactly only if the outcome depends on its
+// candidates: if they give different e4m3 codes of h at the block's scale, or
+// could change the block's amax.
+constexpr float TIE_ULPS = 4.f;
+constexpr float TIE_ABS = 6.f;
+// Uncertain elements listed per work item: 1.6 (decode), 54 (prefill) and 76
+// (skewed batch) on average.  An element beyond the list keeps its nominal
+// rounding.
+constexpr int UNC_CAP = 448;
+
+// bf16 h = bf16(silu(g) * u) for bf16 values g and u, evaluated in fp64
+// (the exact product rounded once).  Not inlined: it runs rarely, and its
+// registers stay out of the epilogue's common path.
+__device__ __noinline__ float silu_mul_exact(float g, float u) {
+  const double gd = (double)g;
+  return bf16_to_f32(f64_to_bf16(gd / (1.0 + exp(-gd)) * (double)u));
+}
+
+// The same in fp32, with the fp64 evaluation where the fp32 product lies
+// within 16 ulps of a bf16 rounding midpoint, or |g| > 64 (where exp(-g)
+// leaves the fp32 range).  exp(-g) = 2^t with t = -g log2(e) split into its
+// fp32 rounding th and the remainder tl (an fma gives the product's rounding
+// error exactly; the constant's own error is added): 2^th is the hardware
+// exp2 (1 ulp) and 2^tl = 1 + tl ln 2 to far below an ulp.  With the
+// hardware reciprocal (1 ulp) and four roundings, the fp32 product is within
+// 5 ulps of silu(g) u.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  constexpr float L2E = 1.44269502f, L2E_LO = 1.92596299e-8f, LN2 = 0.693147182f;
+  const float th = -g * L2E;
+  const float tl = fmaf(-g, L2E, -th) - g * L2E_LO;
+  const float e2 = __builtin_amdgcn_exp2f(th);
+  const float e = fmaf(e2, tl * LN2, e2);
+  const float h = g * __builtin_amdgcn_rcpf(1.f + e) * u;
+  const uint32_t lo = __float_as_uint(h) & 0xFFFFu;
+  if (fabsf((float)lo - 32768.f) <= 16.f || fabsf(g) > 64.f) return silu_mul_exact(g, u);
+  return round_bf16(h);
+}
+
+// One unit in the last place of fp32 value v (the smallest normal's for
+// tiny v).
+__device__ __forceinline__ float ulp32(float v) {
+  const uint32_t e = __float_as_uint(v) & 0x7F800000u;
+  return __uint_as_float(e > (24u << 23) ? e - (23u << 23) : (1u << 23));
+}
+
+// An uncertain element of the up-projection's epilogue (LDS list entry).
+struct UncEntry {
+  int key;              // tile row << 8 | h column
+  int flags;            // UNC_G, UNC_U: g / u uncertain; UNC_NEED: decided exactly
+  float ga, ua;         // the fp32 sums
+  float wg, wu;         // half-widths of their candidate intervals
+  float hnom;           // h from the nominal roundings
+  float hmin, hmax;     // h over the candidates (signed)
+  float gx, ux;         // exact bf16 g and u (recomputed components)
+  float hfin;           // exact h
+};
+enum : int { UNC_G = 1, UNC_U = 2, UNC_NEED = 4 };
+
+// The exact (float64) value of one e4m3 Linear output before its bf16
+// rounding: the dot product of an e4m3 activation row (one scale per 128
+// elements) with an e4m3 weight row (one block scale per 128 inputs).  All
+// 64 lanes of the wave call it.  The 16-element partial sums are exact in
+// float64 (a product of two e4m3 values has at most 8 significant bits and
+// the partial sums span fewer than 53), and each is scaled once by the exact
+// product of its two scales.  A lane's loads of up to CH 16-byte chunks of
+// each row are issued together (one round trip for rows of up to CH * 1024).
+template <int CH>
+__device__ __forceinline__ double exact_row_dot(const uint8_t* xq, const float* xs, const uint8_t* wq, const float* ws,
+                                                int d) {
+  const int lane = threadIdx.x & 63;
+  const int nch = d >> 4;
+  double s = 0.0;
+  for (int c0 = lane; c0 < nch; c0 += 64 * CH) {
+    uint4 xv[CH], wv[CH];
+    float xsv[CH], wsv[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      const int c = min(c0 + 64 * i, nch - 1);  // past the row's end: its last chunk, not used
+      xv[i] = *(const uint4*)(xq + (size_t)c * 16);
+      wv[i] = *(const uint4*)(wq + (size_t)c * 16);
+      xsv[i] = xs[c >> 3];
+      wsv[i] = ws[c >> 3];
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) {
+      if (c0 + 64 * i < nch) {
+        const uint32_t xw[4] = {xv[i].x, xv[i].y, xv[i].z, xv[i].w}, ww[4] = {wv[i].x, wv[i].y, wv[i].z, wv[i].w};
+        double p = 0.0;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const v2bf x0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xw[k], 1.0f, false);
+          const v2bf x1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(xw[k], 1.0f, true);
+          const v2bf w0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[k], 1.0f, false);
+          const v2bf w1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(ww[k], 1.0f, true);
+          p = fma((double)(float)x0[0], (double)(float)w0[0], p);
+          p = fma((double)(float)x0[1], (double)(float)w0[1], p);
+          p = fma((double)(float)x1[0], (double)(float)w1[0], p);
+          p = fma((double)(float)x1[1], (double)(float)w1[1], p);
+        }
+        s = fma(p, (double)xsv[i] * (double)wsv[i], s);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o);
+  return s;
+}
+
+// e4m3 code of h / sc (as the quantiser computes it)
+__device__ __forceinline__ uint32_t e4m3_code(float h, float sc) {
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(h / sc, 0.f, 0, false) & 0xFFu;
+}
+
+// Exact g, u and h of the listed elements whose indices `need` holds, one
+// wave per element.  row_tok: the token of each tile row (LDS); xq, xs: the
+// activation codes and scales (rows by token); w1, w3, s1, s3: the item's
+// gate and up weight rows (its first h column) and their K block scales.
+// CH: 16-byte chunks per lane in flight (fewer where registers are scarce).
+template <int CH>
+__device__ __forceinline__ void recompute_listed(UncEntry* ul, const int* need, int n_need, const int* row_tok,
+                                                 const uint8_t* xq, const float* xs, const uint8_t* w1,
+                                                 const uint8_t* w3, const float* s1, const float* s3, int d) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int nkb = d / BLK;
+  for (int k = wave; k < n_need; k += 8) {
+    const int i = __builtin_amdgcn_readfirstlane(need[k]);
+    const int flags = __builtin_amdgcn_readfirstlane(ul[i].flags);
+    const int key = __builtin_amdgcn_readfirstlane(ul[i].key);
+    const int tok = __builtin_amdgcn_readfirstlane(row_tok[key >> 8]);
+    const uint8_t* xrow = xq + (size_t)tok * d;
+    const float* xsrow = xs + (size_t)tok * nkb;
+    const size_t wofs = (size_t)(key & 255) * d;
+    float gx = ul[i].gx, ux = ul[i].ux;
+    if (flags & UNC_G) gx = bf16_to_f32(f64_to_bf16(exact_row_dot<CH>(xrow, xsrow, w1 + wofs, s1, d)));
+    if (flags & UNC_U) ux = bf16_to_f32(f64_to_bf16(exact_row_dot<CH>(xrow, xsrow, w3 + wofs, s3, d)));
+    if (lane == 0) {
+      ul[i].gx = gx;
+      ul[i].ux = ux;
+      ul[i].hfin = silu_mul_exact(gx, ux);
+    }
+  }
+}
+
 // Up-projection epilogue: h = bf16(silu(bf16 g) * bf16 u) for the wave's 32
-// columns of h block it.blk x its 64 rows; e4m3: per-row amax over the
-// block's 128 columns (4 waves) through `red` (2 KiB of LDS), then e4m3 h
-// and its scale; bf16: h itself.
+// columns of h block it.blk x its 64 rows; e4m3: g, u and h rounded as the
+// exact values round (TIE_ULPS), per-row amax over the block's 128 columns
+// (4 waves) through `red` (2 KiB of LDS) and a list of uncertain elements
+// (up to 22 KiB), then e4m3 h and its scale; bf16: h itself.
 template <int ROWS, bool BF, bool COH, bool SPLIT>
 __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& it,
                                             const v4f (&acc)[2][2][Tile<ROWS>::MVMAX], float* red) {
@@ -578,7 +734,8 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
   const int wr = wave >> 2, wc = wave & 3;
   const int nib = a.I / BLK;
   if constexpr (SPLIT && !BF) {
-    if (a.up_ks > 1 || a.up_stream > 0) {  // fp32 partials of g and u for K slice (plane) it.kslice
+    {  // fp32 partials of g and u for K slice (plane) it.kslice: the split
+       // instances run only when a.up_ks > 1 or a.up_stream > 0
       const size_t R = (size_t)a.T * a.K + a.T;
 #pragma unroll
       for (int m = 0; m < MVX; ++m) {
@@ -622,30 +779,166 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
     }
     return;
   }
+  // g and u as their exact values round (see TIE_ULPS).  LDS after the
+  // stage buffers are retired: the per-wave row amax of the certain elements
+  // (red), three bounds per tile row (row_hi, row_lo, row_fin: uint bits of
+  // non-negative floats, so integer atomicMax orders them), each tile row's
+  // token, the list counts and the uncertain elements (UncEntry).  The list
+  // is worked by one thread per entry, the exact recomputations by whole
+  // waves.
+  uint32_t* row_hi = (uint32_t*)(red + 512);
+  uint32_t* row_lo = row_hi + 128;
+  uint32_t* row_fin = row_lo + 128;
+  int* row_tok = (int*)(row_fin + 128);
+  int* n_unc_p = row_tok + 128;
+  int* n_need_p = n_unc_p + 1;
+  int* need = n_unc_p + 4;  // indices of the entries decided exactly
+  UncEntry* ul = (UncEntry*)(need + UNC_CAP);
+  static_assert(4 * (512 + 4 * 128 + 4 + UNC_CAP) + UNC_CAP * sizeof(UncEntry) <= Tile<ROWS>::template SMEM<false>,
+                "the epilogue's LDS must fit in the stage buffers");
+  if (threadIdx.x < 384) row_hi[threadIdx.x] = 0u;  // row_hi, row_lo, row_fin
+  if (threadIdx.x == 0) n_unc_p[0] = n_unc_p[1] = 0;
+  // the lane that copies tile row 64 w + l's activation scales holds its row
+  // pointer (xs + token * (d / 128), plus the K offset of a split item)
+  if (wave < Tile<ROWS>::SWAVES && wave * 64 + lane < ROWS) row_tok[wave * 64 + lane] = (int)((it.src.s - a.xs) / (a.d / BLK));
+  lds_barrier();
   float hv[2][MVX][4];
+  uint32_t unc = 0;  // bit (jt MVX + m) 4 + j: the element is listed
 #pragma unroll
   for (int m = 0; m < MVX; ++m) {
-    float amax = 0.f;
+    float rmg = 0.f, rmu = 0.f;
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float gv = round_bf16(acc[0][jt][m][j]);
-        const float uv = round_bf16(acc[1][jt][m][j]);
-        const float h = round_bf16(gv / (1.f + expf(-gv)) * uv);
-        hv[jt][m][j] = h;
-        amax = fmaxf(amax, fabsf(h));
+        rmg = fmaxf(rmg, fabsf(acc[0][jt][m][j]));
+        rmu = fmaxf(rmu, fabsf(acc[1][jt][m][j]));
       }
-    amax = fmaxf(amax, __shfl_xor(amax, 16));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    if (g == 0) red[(wr * 4 + wc) * 64 + 16 * m + r] = amax;
+    rmg = fmaxf(rmg, __shfl_xor(rmg, 16));
+    rmg = fmaxf(rmg, __shfl_xor(rmg, 32));
+    rmu = fmaxf(rmu, __shfl_xor(rmu, 16));
+    rmu = fmaxf(rmu, __shfl_xor(rmu, 32));
+    const float eg = TIE_ABS * 0x1p-24f * rmg, eu = TIE_ABS * 0x1p-24f * rmu;
+    const int rr = wr * 64 + 16 * m + r;
+    float cmax = 0.f;  // amax of the certain elements
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float ga = acc[0][jt][m][j], ua = acc[1][jt][m][j];
+        const float g0 = round_bf16(ga), u0 = round_bf16(ua);
+        const float h = silu_mul(g0, u0);
+        hv[jt][m][j] = h;
+        // half-widths of the intervals that hold the exact sums; a row whose
+        // sums here are all zero is zero
+        const float qg = ulp32(ga), qu = ulp32(ua);
+        const float wg = TIE_ULPS * qg + eg, wu = TIE_ULPS * qu + eu;
+        const float dg = fabsf((float)(__float_as_uint(ga) & 0xFFFFu) - 32768.f) * qg;
+        const float du = fabsf((float)(__float_as_uint(ua) & 0xFFFFu) - 32768.f) * qu;
+        const bool cg = rr < it.nrows && rmg > 0.f && dg <= wg;
+        const bool cu = rr < it.nrows && rmu > 0.f && du <= wu;
+        if (cg || cu) {
+          const int slot = atomicAdd(n_unc_p, 1);
+          if (slot < UNC_CAP) {
+            unc |= 1u << ((jt * MVX + m) * 4 + j);
+            UncEntry& e = ul[slot];
+            e.key = (rr << 8) | (wc * 32 + jt * 16 + 4 * g + j);
+            e.flags = (cg ? UNC_G : 0) | (cu ? UNC_U : 0);
+            e.ga = ga;
+            e.ua = ua;
+            e.wg = wg + 2.f * qg;  // margin for the fp32 arithmetic of the interval ends
+            e.wu = wu + 2.f * qu;
+            continue;
+          }
+        }
+        if (rr < it.nrows) cmax = fmaxf(cmax, fabsf(h));
+      }
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
+    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    if (g == 0) red[(wr * 4 + wc) * 64 + 16 * m + r] = cmax;
   }
   lds_barrier();
+  const int n_unc = min(__builtin_amdgcn_readfirstlane(*n_unc_p), UNC_CAP);
+  int n_need = 0;
+  if (n_unc > 0) {  // uniform over the workgroup
+    // h over each element's candidates, and the bounds of its row's amax
+    for (int i = threadIdx.x; i < n_unc; i += blockDim.x) {
+      UncEntry& e = ul[i];
+      const float g0 = round_bf16(e.ga), u0 = round_bf16(e.ua);
+      const float glo = (e.flags & UNC_G) ? round_bf16(e.ga - e.wg) : g0;
+      const float ghi = (e.flags & UNC_G) ? round_bf16(e.ga + e.wg) : g0;
+      const float ulo = (e.flags & UNC_U) ? round_bf16(e.ua - e.wu) : u0;
+      const float uhi = (e.flags & UNC_U) ? round_bf16(e.ua + e.wu) : u0;
+      const float c0 = silu_mul(glo, ulo), c1 = silu_mul(glo, uhi), c2 = silu_mul(ghi, ulo), c3 = silu_mul(ghi, uhi);
+      const float hmin = fminf(fminf(c0, c1), fminf(c2, c3)), hmax = fmaxf(fmaxf(c0, c1), fmaxf(c2, c3));
+      e.hnom = e.hfin = silu_mul(g0, u0);  // as the owning lane holds it
+      e.gx = g0;
+      e.ux = u0;
+      // h is linear in u and monotone in g away from silu's minimum (g near
+      // -1.28): corners bound it; an interval of g that holds more than two
+      // bf16 values around that minimum is decided exactly
+      const bool wide_min = (e.flags & UNC_G) && glo < -1.2f && ghi > -1.36f &&
+                            (__float_as_uint(ghi) - __float_as_uint(glo)) > 0x10000u;
+      e.hmin = hmin;
+      e.hmax = hmax;
+      if (wide_min) e.flags |= UNC_NEED;
+      const float lo = (hmin <= 0.f && hmax >= 0.f) ? 0.f : fminf(fabsf(hmin), fabsf(hmax));
+      const float hi = wide_min ? INFINITY : fmaxf(fabsf(hmin), fabsf(hmax));
+      const int row = e.key >> 8;
+      atomicMax(&row_hi[row], __float_as_uint(hi));
+      atomicMax(&row_lo[row], __float_as_uint(lo));
+    }
+    lds_barrier();
+    // an element is decided exactly when its row's amax is not settled or its
+    // candidates give different e4m3 codes at the row's scale
+    for (int i = threadIdx.x; i < n_unc; i += blockDim.x) {
+      UncEntry& e = ul[i];
+      const int row = e.key >> 8, wrr = row >> 6;
+      float cert = 0.f;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) cert = fmaxf(cert, red[(wrr * 4 + c) * 64 + (row & 63)]);
+      const float alo = fmaxf(cert, __uint_as_float(row_lo[row])), ahi = fmaxf(cert, __uint_as_float(row_hi[row]));
+      const float sc = alo == 0.f ? 1.f : alo / E4M3_MAX;
+      if (ahi > alo || e4m3_code(e.hmin, sc) != e4m3_code(e.hmax, sc)) e.flags |= UNC_NEED;
+      if (e.flags & UNC_NEED) need[atomicAdd(n_need_p, 1)] = i;
+    }
+    lds_barrier();
+    n_need = __builtin_amdgcn_readfirstlane(*n_need_p);
+    if (n_need > 0) {  // rare: the exact values, kept out of line
+      const bool sh = it.expert >= a.E;
+      const ExpertPtrs& P = sh ? a.shared : a.routed;
+      const size_t wofs = ((sh ? 0 : (size_t)it.expert) * a.I + (size_t)it.blk * BLK) * a.d;
+      recompute_listed<ROWS == 32 ? 4 : 8>(ul, need, n_need, row_tok, a.xq, a.xs, P.w1 + wofs, P.w3 + wofs, it.sa0, it.sa1, a.d);
+      lds_barrier();
+      // the rows' amax over the final values of their uncertain elements
+      for (int i = threadIdx.x; i < n_unc; i += blockDim.x)
+        atomicMax(&row_fin[ul[i].key >> 8], __float_as_uint(fabsf(ul[i].hfin)));
+      lds_barrier();
+      if (unc) {  // this lane's listed elements take their final values
+        for (int k = 0; k < n_need; ++k) {
+          const int i = need[k];
+          const int key = ul[i].key;
+          const float hf = ul[i].hfin;
+#pragma unroll
+          for (int m = 0; m < MVX; ++m)
+#pragma unroll
+            for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+                if (key == (((wr * 64 + 16 * m + r) << 8) | (wc * 32 + jt * 16 + 4 * g + j))) hv[jt][m][j] = hf;
+        }
+      }
+    }
+  }
+  // A row's amax: its certain elements' and, with no exact recomputation in
+  // the tile, its settled lower bound (the bounds of every uncertain element's
+  // row then coincide, and hold its nominal h); else the final values'.
+  const uint32_t* row_unc = n_need > 0 ? row_fin : row_lo;
 #pragma unroll
   for (int m = 0; m < MVX; ++m) {
     const int rr = wr * 64 + 16 * m + r;
     if (rr < it.nrows) {
-      float amax = 0.f;
+      float amax = n_unc > 0 ? __uint_as_float(row_unc[rr]) : 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) amax = fmaxf(amax, red[(wr * 4 + c) * 64 + 16 * m + r]);
       const float sc = amax == 0.f ? 1.f : amax / E4M3_MAX;

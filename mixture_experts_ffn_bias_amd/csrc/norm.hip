@@ -16,20 +16,6 @@ namespace moe {
 
 namespace {
 
-// bf16 nearest (ties to even) of a double, rounded once: the conversion to
-// float rounds to odd (inexact results get their last bit set), which keeps
-// the following round-to-nearest-even to bf16 correct.
-__device__ __forceinline__ uint16_t f64_to_bf16(double v) {
-  float f = (float)v;
-  const double back = (double)f;
-  if (back != v) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 1u) == 0u) u += ((back < v) == (f >= 0.f)) ? 1u : 0xFFFFFFFFu;
-    f = __uint_as_float(u);
-  }
-  return f32_to_bf16(f);
-}
-
 constexpr int NORM_THREADS = 256;
 
 // NCH 8-element chunks per thread (d <= 256 * 8 * NCH).  Every load of the

@@ -297,6 +297,33 @@ def test_add_rmsnorm(T, d):
     assert np.array_equal(got, hn_ref)                          # normalised rows: bit-exact
 
 
+def test_add_rmsnorm_products_below_float_range():
+    """Gains so small that gain * r / rms lies below half the smallest float32
+    subnormal (the float conversion gives a signed zero), at the subnormal
+    boundary, and in the bf16 subnormal range: each output is the oracle's
+    (a signed zero of the product's sign, never NaN)."""
+    _say("moe_add_rmsnorm products below the float32 range")
+    d, T = 512, 6
+    g = torch.Generator(device=DEV).manual_seed(11)
+    x = torch.randn((T, d), generator=g, device=DEV).to(torch.bfloat16)
+    res = torch.randn((T, d), generator=g, device=DEV).to(torch.bfloat16)
+    tiny = np.array([1.4e-45, -1.4e-45, 2.8e-45, -4.2e-45, 1e-42, -1e-40, 3e-39, -1.2e-38], dtype=np.float32)
+    gain = torch.from_numpy(np.resize(tiny, d)).to(DEV)
+    hn_ref, res_ref = oracle.add_rmsnorm(f64(x), f64(res), gain.cpu().numpy())
+    out = torch.empty_like(x)
+    moe.moe_add_rmsnorm(d, T, x, res, gain, 1e-6, out)
+    torch.cuda.synchronize()
+    got = f64(out)
+    n_nan = int(np.isnan(got).sum())
+    diff = np.flatnonzero(got != hn_ref)
+    print(f"[parity] add_rmsnorm tiny gains: {n_nan} NaN, {diff.size} of {got.size} values differ", flush=True)
+    assert n_nan == 0 and diff.size == 0
+    assert np.array_equal(f64(res), res_ref)
+    ref_sign = np.signbit(hn_ref)
+    got_sign = np.signbit(got)
+    assert np.array_equal(got_sign, ref_sign)                    # zeros keep the product's sign
+
+
 def test_add_rmsnorm_in_place_output():
     _say("moe_add_rmsnorm out aliases x")
     d, T = 512, 9
