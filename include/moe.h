@@ -202,6 +202,26 @@ int moe_forward(const moe_dims* dims, const moe_weights* weights, int64_t tokens
                 const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the device array that moe_forward_no_workspace uses in place of a
+ * workspace (one per GPU the library runs on, held until the process ends). */
+#define MOE_STATIC_WORKSPACE_BYTES ((size_t)32 << 20)
+
+/* moe_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same arguments and the same result as moe_forward, without a workspace
+ * argument.  The workspace is a file-scope device array of
+ * MOE_STATIC_WORKSPACE_BYTES on each GPU (its address is looked up once per
+ * device, on the first call with that device current); the call allocates
+ * nothing.  tokens must satisfy moe_workspace_size(dims, tokens) <=
+ * MOE_STATIC_WORKSPACE_BYTES (up to 181 tokens at the DeepSeek-V3.2-Exp
+ * shape), else MOE_ERR_UNSUPPORTED is returned before anything runs.  Every
+ * call on one GPU uses that GPU's array: calls that overlap in time on one GPU
+ * (other streams, other threads) race and give undefined results; order them.
+ * No part of the array needs to start zeroed. */
+int moe_forward_no_workspace(const moe_dims* dims, const moe_weights* weights, int64_t tokens,
+                             const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
+                             void* stream);
+
 /* Number of events moe_forward_timed records. */
 #define MOE_FORWARD_EVENTS 6
 

@@ -20,10 +20,11 @@ MOE_OK = 0
 SYMBOLS = ("moe_workspace_size", "moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_bf16", "moe_combine",
            "moe_forward", "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_forward_shard",
            "moe_forward_fused_workspace_size", "moe_forward_fused", "moe_forward_fused_status", "moe_add_rmsnorm",
-           "moe_mlp_workspace_size", "moe_mlp", "moe_status_string")
+           "moe_mlp_workspace_size", "moe_mlp", "moe_forward_no_workspace", "moe_status_string")
 MOE_ERR_STALLED = -6
 FUSED_MAX_TOKENS = 64
 MOE_FORWARD_EVENTS = 6
+MOE_STATIC_WORKSPACE_BYTES = 32 << 20
 
 
 class MoeError(RuntimeError):
@@ -92,9 +93,11 @@ def lib() -> ctypes.CDLL:
         L.moe_mlp_workspace_size.argtypes = [i32, i32, i64]
         L.moe_mlp_workspace_size.restype = sz
         L.moe_mlp.argtypes = [i32, i32, i64, ctypes.POINTER(moe_experts), vp, vp, vp, sz, vp]
+        L.moe_forward_no_workspace.argtypes = [dp, ctypes.POINTER(moe_weights), i64, vp, vp, vp, vp, vp]
         for n in ("moe_gate", "moe_permute", "moe_grouped_ffn", "moe_grouped_ffn_bf16", "moe_combine", "moe_forward",
                   "moe_forward_timed", "moe_forward_bf16", "moe_forward_bf16_timed", "moe_forward_shard",
-                  "moe_forward_fused", "moe_forward_fused_status", "moe_add_rmsnorm", "moe_mlp"):
+                  "moe_forward_fused", "moe_forward_fused_status", "moe_add_rmsnorm", "moe_mlp",
+                  "moe_forward_no_workspace"):
             getattr(L, n).restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -186,6 +189,13 @@ def moe_forward(dims, weights: moe_weights, tokens, x, delta, idx_out, w_out, ws
     _check(lib().moe_forward(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta), _p(idx_out),
                              _p(w_out), _p(ws), ws.numel() if ws is not None else 0, _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_no_workspace(dims, weights: moe_weights, tokens, x, delta, idx_out, w_out, stream=None):
+    """moe_forward with the library's own per-GPU array as its workspace (allocates nothing;
+    calls that overlap on one GPU race)."""
+    _check(lib().moe_forward_no_workspace(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta),
+                                          _p(idx_out), _p(w_out), _stream(stream)), "moe_forward_no_workspace")
 
 
 def moe_forward_timed(dims, weights: moe_weights, tokens, x, delta, idx_out, w_out, ws, events, stream=None):

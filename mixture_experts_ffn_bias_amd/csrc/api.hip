@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "common.h"
@@ -458,6 +459,48 @@ int moe_forward_shard(const moe_dims* dims, const moe_weights* weights, int64_t 
                                 expert_begin, expert_end)));
   return hip_status(launch_combine_partial(idx, w, pair_row, rows, with_shared ? 1 : 0, T, d.topk, expert_begin,
                                            expert_end, d.d_model, y_partial, s));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The workspace of moe_forward_no_workspace: one array per GPU, for callers
+// that cannot allocate.  In host code `scratch` names a host-side stand-in;
+// its device address comes from hipGetSymbolAddress, looked up once per
+// device with that device current and kept in scratch_dev.
+static __device__ __align__(256) uint8_t scratch[MOE_STATIC_WORKSPACE_BYTES];
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_dev[SCRATCH_MAX_DEVICES] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    scratch_dev[dev] = p;
+  }
+  *out = scratch_dev[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward_no_workspace(const moe_dims* dims, const moe_weights* weights, int64_t tokens, const uint16_t* x,
+                             uint16_t* delta, int32_t* idx_out, float* w_out, void* stream) {
+  MOE_TRY(check_dims(dims));
+  MOE_TRY(check_tokens(*dims, tokens));
+  if (tokens == 0) return MOE_OK;
+  if (layout(*dims, tokens).total > MOE_STATIC_WORKSPACE_BYTES) return MOE_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  MOE_TRY(scratch_address(&ws));
+  return forward_fp8(dims, weights, tokens, x, delta, idx_out, w_out, ws, MOE_STATIC_WORKSPACE_BYTES,
+                     (hipStream_t)stream, nullptr);
 }
 
 size_t moe_forward_fused_workspace_size(const moe_dims* dims, int64_t tokens) {

@@ -236,3 +236,17 @@ def test_fused_argument_checks():
     noshared = moe.moe_weights(FAKE, FAKE, ex, moe.moe_experts(None, None, None, None, None, None))
     assert call(wt=ctypes.byref(noshared)) == -1
     assert L.moe_forward_fused_status(None, None) == -1
+
+
+def test_no_workspace_forward_argument_checks():
+    # checked on the host before the device array is looked up or anything runs
+    L = moe.lib()
+    w = B.moe_weights()
+    assert L.moe_forward_no_workspace(None, ctypes.byref(w), 4, FAKE, FAKE, None, None, None) == -1
+    assert L.moe_forward_no_workspace(ctypes.byref(dims()), ctypes.byref(w), -1, FAKE, FAKE, None, None, None) == -1
+    assert L.moe_forward_no_workspace(ctypes.byref(dims()), ctypes.byref(w), 0, FAKE, FAKE, None, None, None) == 0
+    big = 1
+    while moe.moe_workspace_size(dims(), big) <= moe.MOE_STATIC_WORKSPACE_BYTES:
+        big *= 2
+    assert L.moe_forward_no_workspace(ctypes.byref(dims()), ctypes.byref(w), big, FAKE, FAKE, None, None, None) == -2
+    assert moe.moe_workspace_size(dims(), 64) <= moe.MOE_STATIC_WORKSPACE_BYTES
