@@ -258,6 +258,9 @@ def gpu_info(torch):
     p = torch.cuda.get_device_properties(0)
     info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
             "hbm_GiB": round(p.total_memory / 2 ** 30, 1)}
+    if "rocprof" in os.environ.get("LD_PRELOAD", ""):
+        info["clocks"] = None  # under the profiler a child may not start another program (rocm-smi)
+        return info
     try:
         out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=10).stdout
         clk = {}
