@@ -573,14 +573,15 @@ __device__ __forceinline__ int item_mvalid(const Item<ROWS>& it) {
 // sum of d / 128 scaled block products.  Its error is a few units of 2^-24
 // times the size of the partial sums (measured against the exact sums on the
 // CPU: median 0.5, 99.99th percentile 7, largest 12 units of 2^-24 x the
-// largest |sum| of the row among a wave's 32 columns), so when the exact value lies
-// near a bf16 rounding midpoint the fp32 sum may round to the other
-// neighbour.  A sum is "uncertain" when it lies within TIE_ULPS of its own
-// ulps plus TIE_ABS x 2^-24 x that row maximum of a midpoint; the bf16 values
-// that an interval of that width around it rounds to are its candidates.  An
-// uncertain element is recomputed exactly only if the outcome depends on its
-// candidates: if they give different e4m3 codes of h at the block's scale, or
-// could change the block's amax.
+// largest |sum| of the row among a wave's 32 columns), so when the exact
+// value lies near a bf16 rounding midpoint the fp32 sum may round to the
+// other neighbour.  A sum v is "uncertain" when it lies within TIE_ULPS x |v|
+// x 2^-23 (at least TIE_ULPS of its ulps) plus TIE_ABS x 2^-24 x that row
+// maximum of a midpoint; the bf16 values that an interval of that width
+// around it rounds to are its candidates.  An uncertain element is
+// recomputed exactly only if the outcome depends on its candidates: if they
+// give different e4m3 codes of h at the block's scale, or could change the
+// block's amax.
 constexpr float TIE_ULPS = 4.f;
 constexpr float TIE_ABS = 6.f;
 // Uncertain elements listed per work item: 1.6 (decode), 54 (prefill) and 76
@@ -614,13 +615,6 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   const uint32_t lo = __float_as_uint(h) & 0xFFFFu;
   if (fabsf((float)lo - 32768.f) <= 16.f || fabsf(g) > 64.f) return silu_mul_exact(g, u);
   return round_bf16(h);
-}
-
-// One unit in the last place of fp32 value v (the smallest normal's for
-// tiny v).
-__device__ __forceinline__ float ulp32(float v) {
-  const uint32_t e = __float_as_uint(v) & 0x7F800000u;
-  return __uint_as_float(e > (24u << 23) ? e - (23u << 23) : (1u << 23));
 }
 
 // An uncertain element of the up-projection's epilogue (LDS list entry).
@@ -802,10 +796,11 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
   // pointer (xs + token * (d / 128), plus the K offset of a split item)
   if (wave < Tile<ROWS>::SWAVES && wave * 64 + lane < ROWS) row_tok[wave * 64 + lane] = (int)((it.src.s - a.xs) / (a.d / BLK));
   lds_barrier();
-  float hv[2][MVX][4];
+  float hv[2][MVX][4] = {};
   uint32_t unc = 0;  // bit (jt MVX + m) 4 + j: the element is listed
 #pragma unroll
   for (int m = 0; m < MVX; ++m) {
+    if (wr * 64 + 16 * m >= it.nrows) continue;  // a sub-tile without rows (wave-uniform)
     float rmg = 0.f, rmu = 0.f;
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
@@ -829,14 +824,14 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
         const float g0 = round_bf16(ga), u0 = round_bf16(ua);
         const float h = silu_mul(g0, u0);
         hv[jt][m][j] = h;
-        // half-widths of the intervals that hold the exact sums; a row whose
-        // sums here are all zero is zero
-        const float qg = ulp32(ga), qu = ulp32(ua);
-        const float wg = TIE_ULPS * qg + eg, wu = TIE_ULPS * qu + eu;
-        const float dg = fabsf((float)(__float_as_uint(ga) & 0xFFFFu) - 32768.f) * qg;
-        const float du = fabsf((float)(__float_as_uint(ua) & 0xFFFFu) - 32768.f) * qu;
-        const bool cg = rr < it.nrows && rmg > 0.f && dg <= wg;
-        const bool cu = rr < it.nrows && rmu > 0.f && du <= wu;
+        // distance to the nearer bf16 rounding midpoint (the one between the
+        // two bf16 values around the sum; the subtraction is exact) against
+        // the half-width of the interval that holds the exact sum (|v| 2^-23
+        // is at least one ulp of v)
+        const float dg = fabsf(ga - __uint_as_float((__float_as_uint(ga) & 0xFFFF0000u) | 0x8000u));
+        const float du = fabsf(ua - __uint_as_float((__float_as_uint(ua) & 0xFFFF0000u) | 0x8000u));
+        const bool cg = rr < it.nrows && dg <= fmaf(fabsf(ga), TIE_ULPS * 0x1p-23f, eg);
+        const bool cu = rr < it.nrows && du <= fmaf(fabsf(ua), TIE_ULPS * 0x1p-23f, eu);
         if (cg || cu) {
           const int slot = atomicAdd(n_unc_p, 1);
           if (slot < UNC_CAP) {
@@ -846,8 +841,9 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
             e.flags = (cg ? UNC_G : 0) | (cu ? UNC_U : 0);
             e.ga = ga;
             e.ua = ua;
-            e.wg = wg + 2.f * qg;  // margin for the fp32 arithmetic of the interval ends
-            e.wu = wu + 2.f * qu;
+            // plus a margin for the fp32 arithmetic of the interval ends
+            e.wg = fmaf(fabsf(ga), (TIE_ULPS + 2.f) * 0x1p-23f, eg);
+            e.wu = fmaf(fabsf(ua), (TIE_ULPS + 2.f) * 0x1p-23f, eu);
             continue;
           }
         }
