@@ -598,7 +598,7 @@ __device__ __noinline__ float silu_mul_exact(float g, float u) {
 }
 
 // The same in fp32, with the fp64 evaluation where the fp32 product lies
-// within 16 ulps of a bf16 rounding midpoint, or |g| > 64 (where exp(-g)
+// within 8 ulps of a bf16 rounding midpoint, or |g| > 64 (where exp(-g)
 // leaves the fp32 range).  exp(-g) = 2^t with t = -g log2(e) split into its
 // fp32 rounding th and the remainder tl (an fma gives the product's rounding
 // error exactly; the constant's own error is added): 2^th is the hardware
@@ -613,8 +613,24 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   const float e = fmaf(e2, tl * LN2, e2);
   const float h = g * __builtin_amdgcn_rcpf(1.f + e) * u;
   const uint32_t lo = __float_as_uint(h) & 0xFFFFu;
-  if (fabsf((float)lo - 32768.f) <= 16.f || fabsf(g) > 64.f) return silu_mul_exact(g, u);
+  if (fabsf((float)lo - 32768.f) <= 8.f || fabsf(g) > 64.f) return silu_mul_exact(g, u);
   return round_bf16(h);
+}
+
+// Maximum of a non-negative float over lanes l, l ^ 16, l ^ 32 and l ^ 48
+// (one row of an MFMA accumulator tile): two gfx950 lane-swap instructions
+// instead of LDS permutes.  With both operands equal, permlane16_swap leaves
+// rows (0, 0, 2, 2) and (1, 1, 3, 3) of the value in its two results and
+// permlane32_swap the halves (lo, lo) and (hi, hi), so each pairwise maximum
+// is the maximum with the partner lane.  Non-negative floats order as their
+// bits.
+typedef unsigned int v2u32 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float rowmax_nonneg(float v) {
+  uint32_t b = __float_as_uint(v);
+  v2u32 t = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  b = max(t[0], t[1]);
+  t = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __uint_as_float(max(t[0], t[1]));
 }
 
 // An uncertain element of the up-projection's epilogue (LDS list entry).
@@ -809,10 +825,8 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
         rmg = fmaxf(rmg, fabsf(acc[0][jt][m][j]));
         rmu = fmaxf(rmu, fabsf(acc[1][jt][m][j]));
       }
-    rmg = fmaxf(rmg, __shfl_xor(rmg, 16));
-    rmg = fmaxf(rmg, __shfl_xor(rmg, 32));
-    rmu = fmaxf(rmu, __shfl_xor(rmu, 16));
-    rmu = fmaxf(rmu, __shfl_xor(rmu, 32));
+    rmg = rowmax_nonneg(rmg);
+    rmu = rowmax_nonneg(rmu);
     const float eg = TIE_ABS * 0x1p-24f * rmg, eu = TIE_ABS * 0x1p-24f * rmu;
     const int rr = wr * 64 + 16 * m + r;
     float cmax = 0.f;  // amax of the certain elements
@@ -849,8 +863,7 @@ __device__ __forceinline__ void up_epilogue(const FfnArgs& a, const Item<ROWS>& 
         }
         if (rr < it.nrows) cmax = fmaxf(cmax, fabsf(h));
       }
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 16));
-    cmax = fmaxf(cmax, __shfl_xor(cmax, 32));
+    cmax = rowmax_nonneg(cmax);
     if (g == 0) red[(wr * 4 + wc) * 64 + 16 * m + r] = cmax;
   }
   lds_barrier();
