@@ -113,7 +113,7 @@ __device__ void dec_signal(int* ctl, int i) {
 // Tile-list entry of the shared expert's tile j (as the plan writes it).
 __device__ int4 shared_tile(const DecodeArgs& a, int j) {
   const FfnArgs& f = a.f;
-  return make_int4(f.E, f.T * f.K + j * DEC_ROWS, min(DEC_ROWS, f.T - j * DEC_ROWS), a.nsh == 1 ? 1 : 0);
+  return make_int4(f.E, f.T * f.K + j * DEC_ROWS, min(DEC_ROWS, f.T - j * DEC_ROWS), (j << 1) | (a.nsh == 1 ? 1 : 0));
 }
 
 // The next item of a range from its counter (every workgroup of the range

@@ -492,7 +492,7 @@ __device__ __forceinline__ void up_item_of(const FfnArgs& a, int4 td, int ib, It
   it.expert = e;
   it.row0 = row0;
   it.nrows = nrows;
-  it.once = td.w != 0;
+  it.once = (td.w & 1) != 0;
   it.nkb = nkb;
   it.kslice = 0;
 }
@@ -539,7 +539,7 @@ __device__ __forceinline__ void down_item_of(const FfnArgs& a, int4 td, int ob, 
   it.expert = e;
   it.row0 = row0;
   it.nrows = nrows;
-  it.once = td.w != 0;
+  it.once = (td.w & 1) != 0;
   it.nkb = nkb;
   it.kslice = 0;
 }
@@ -556,8 +556,13 @@ __device__ __forceinline__ bool down_item(const FfnArgs& a, int item, Item<ROWS>
   const int tile = item / per_tile;
   const int rem = item - tile * per_tile;
   if (tile >= *a.n_tiles || rem >= nob2 * ks) return false;
-  const int ob = rem / ks;
-  down_item_of<ROWS, BF>(a, a.tiles[tile], ob, it);
+  // without split K, tile k of an expert starts its output pairs k (nob2 % 8)
+  // further on: items go round-robin over the 8 XCDs, so the item of tile
+  // k + 1 that reads a pair's w2 rows then runs on the XCD, and at about the
+  // time, of the item of tile k that read them, and that XCD's L2 holds them
+  const int4 td = a.tiles[tile];
+  const int ob = ks > 1 ? rem / ks : (rem + (td.w >> 1) * (nob2 & 7)) % nob2;
+  down_item_of<ROWS, BF>(a, td, ob, it);
   if (ks > 1) item_kslice<ROWS, BF>(it, rem - ob * ks, a.dn_kper);
   return true;
 }

@@ -1,5 +1,6 @@
 // The FFN tile list, built by one 256-thread workgroup (kernels.h, launch_ffn:
-// tiles[i] = {expert, first row, rows, once}).  Used by the plan kernel and,
+// tiles[i] = {expert, first row, rows, (k << 1) | once}: k the tile's index
+// within its expert, once = 1 for an expert's only tile).  Used by the plan kernel and,
 // for small batches, by the single-launch permutation, which has the expert
 // offsets at hand already.
 #pragma once
@@ -13,7 +14,7 @@ namespace moe {
 // Tile j of the shared expert (number e_sh, permuted rows [TK, TK + T), nsh
 // tiles): NT rows each in row order, the last one ragged.
 __device__ __forceinline__ uint4 shared_tile(int j, int T, int TK, int NT, int nsh, int e_sh) {
-  return make_uint4(e_sh, TK + j * NT, min(NT, T - j * NT), nsh == 1 ? 1 : 0);
+  return make_uint4(e_sh, TK + j * NT, min(NT, T - j * NT), (j << 1) | (nsh == 1 ? 1 : 0));
 }
 
 // Thread e (0..255) brings expert e's permuted rows [lo, lo + cnt) (ignored
@@ -48,7 +49,7 @@ __device__ __forceinline__ void plan_tiles_block(int lo, int cnt, int T, int K, 
   const int base = act ? s[e] - n : 0;
   const int rt = n > 1 ? min(NT, ((cnt + n - 1) / n + 15) / 16 * 16) : NT;
   for (int j = 0; j < n && base + j < cap; ++j)
-    st16<COH>(tiles + nsh + base + j, make_uint4(e - e_lo, lo + j * rt, min(rt, cnt - j * rt), n == 1 ? 1 : 0));
+    st16<COH>(tiles + nsh + base + j, make_uint4(e - e_lo, lo + j * rt, min(rt, cnt - j * rt), (j << 1) | (n == 1 ? 1 : 0)));
   if (threadIdx.x == 0) st<COH>(n_tiles, (int32_t)(nsh + min(s[255], cap)));
 }
 
