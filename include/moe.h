@@ -228,8 +228,11 @@ int moe_forward_no_workspace(const moe_dims* dims, const moe_weights* weights, i
 /* moe_forward that also records stage_events[0..5] (hipEvent_t handles the
  * caller created, host array) on `stream`: before the gate, before the
  * permutation, before the up-projection (w1/w3, SwiGLU, h quantisation),
- * before the down-projection (w2), before the combine, and after it.  For
- * per-kernel timing; the computation is identical to moe_forward. */
+ * before the down-projection (w2), before the combine, and after it.  A NULL
+ * entry is not recorded (each recorded event adds a little time to the
+ * step, so a caller times only the stages it needs); a NULL array is
+ * MOE_ERR_INVALID_ARG.  For per-kernel timing; the computation is identical
+ * to moe_forward. */
 int moe_forward_timed(const moe_dims* dims, const moe_weights* weights, int64_t tokens,
                       const uint16_t* x, uint16_t* delta, int32_t* idx_out, float* w_out,
                       void* workspace, size_t workspace_bytes, void* stream,

@@ -199,7 +199,7 @@ def moe_forward_no_workspace(dims, weights: moe_weights, tokens, x, delta, idx_o
 
 
 def moe_forward_timed(dims, weights: moe_weights, tokens, x, delta, idx_out, w_out, ws, events, stream=None):
-    """events: MOE_FORWARD_EVENTS hipEvent_t handles (ints), e.g. from HipEvents."""
+    """events: MOE_FORWARD_EVENTS hipEvent_t handles (ints, e.g. from HipEvents); None entries are not recorded."""
     arr = (ctypes.c_void_p * MOE_FORWARD_EVENTS)(*events)
     _check(lib().moe_forward_timed(ctypes.byref(dims), ctypes.byref(weights), int(tokens), _p(x), _p(delta),
                                    _p(idx_out), _p(w_out), _p(ws), ws.numel() if ws is not None else 0,

@@ -331,11 +331,11 @@ int forward_impl(const moe_dims* dims, const float* gate_w, const float* gate_b,
   uint8_t* xq = bf16 ? nullptr : at<uint8_t>(workspace, L.xq);
   float* xs = bf16 ? nullptr : at<float>(workspace, L.xs);
   uint16_t* rows = at<uint16_t>(workspace, L.rows);
-  if (ev) (void)hipEventRecord(ev[0], s);
+  record_event(ev, 0, s);
   MOE_TRY(hip_status(launch_gate(x, gate_w, gate_b, T, d.d_model, d.n_experts, d.n_groups, d.topk_groups, d.topk,
                                  d.route_scale, at<float>(workspace, L.zpart),
                                  gate_ksplit(tokens, d.d_model, d.n_experts), idx, w, s)));
-  if (ev) (void)hipEventRecord(ev[1], s);
+  record_event(ev, 1, s);
   // small batches: the permutation kernel also writes the FFN tile list
   const PlanArgs plan{at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles), ffn_tile_rows(tokens), 1,
                       ffn_plan_cap(tokens, d.topk, d.n_experts, true)};
@@ -349,7 +349,7 @@ int forward_impl(const moe_dims* dims, const float* gate_w, const float* gate_b,
                                 bf16 ? nullptr : at<float>(workspace, L.hs), rows, s, ev ? ev + 2 : nullptr, bf16, 0,
                                 -1, planned)));
   const int st = hip_status(launch_combine(idx, w, pair_row, rows, 1, T, d.topk, d.n_experts, d.d_model, delta, s));
-  if (ev) (void)hipEventRecord(ev[5], s);
+  record_event(ev, 5, s);
   return st;
 }
 
@@ -368,10 +368,7 @@ int forward_bf16(const moe_dims* dims, const moe_weights_bf16* weights, int64_t 
 
 int take_events(void* const* stage_events, hipEvent_t* ev) {
   if (!stage_events) return MOE_ERR_INVALID_ARG;
-  for (int i = 0; i < MOE_FORWARD_EVENTS; ++i) {
-    if (!stage_events[i]) return MOE_ERR_INVALID_ARG;
-    ev[i] = (hipEvent_t)stage_events[i];
-  }
+  for (int i = 0; i < MOE_FORWARD_EVENTS; ++i) ev[i] = (hipEvent_t)stage_events[i];  // NULL: not recorded
   return MOE_OK;
 }
 

@@ -148,7 +148,7 @@ hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipE
                          ? ((int64_t)(a.T + ROWS - 1) / ROWS * (a.I / BLK) * (a.d / BLK) + a.up_stream - 1) / a.up_stream
                          : max_tiles * items_per_tile(a.I / BLK, a.up_ks);
   const int64_t g2 = max_tiles * items_per_tile((a.d / BLK + 1) / 2, a.dn_ks);
-  if (ev) (void)hipEventRecord(ev[0], s);
+  record_event(ev, 0, s);
   if (!BF && a.up_stream > 0) {
     if constexpr (ROWS == 32)
       return hipErrorInvalidValue;  // the host picks stream-K for 64- and 128-row tiles only
@@ -168,7 +168,7 @@ hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipE
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  if (ev) (void)hipEventRecord(ev[1], s);
+  record_event(ev, 1, s);
   if (!BF && a.dn_ks > 1)
     hipLaunchKernelGGL((ffn_tiled_kernel<false, ROWS, false, true>), dim3((unsigned)g2), dim3(512), 0, s, a);
   else
@@ -180,7 +180,7 @@ hipError_t launch_gemms(const FfnArgs& a, int64_t max_tiles, hipStream_t s, hipE
                        R, a.d, a.out);
     err = hipGetLastError();
   }
-  if (ev) (void)hipEventRecord(ev[2], s);
+  record_event(ev, 2, s);
   return err;
 }
 

@@ -48,13 +48,19 @@ hipError_t launch_permute(const int32_t* idx, const uint16_t* x, int T, int d, i
 hipError_t launch_quant(const uint16_t* x, int64_t T, int d, uint8_t* xq, float* xs, hipStream_t s,
                         const PlanArgs* dense_plan = nullptr);
 
+// Record ev[i] on s unless the array or that entry is NULL (stage timing).
+inline void record_event(hipEvent_t* ev, int i, hipStream_t s) {
+  if (ev && ev[i]) (void)hipEventRecord(ev[i], s);
+}
+
 // ffn.hip
 int ffn_tile_rows(int64_t T, bool dense = false);   // rows per FFN tile for this token count (dense: the MLP)
 int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
 // E = K = 0 with `shared` set and row_token NULL runs one dense expert over
 // rows 0..T-1 (offsets is then not read).
 // ev: NULL, or three events recorded before the up-projection, before the
-// down-projection and after it (the tile plan precedes ev[0]).
+// down-projection and after it (the tile plan precedes ev[0]); a NULL entry
+// is not recorded.
 // bf16: the expert weights are bf16 without scales; xq is then the bf16
 // input x, hq receives bf16 h ([rows][I]) and xs, hs and the scale pointers
 // are unused.

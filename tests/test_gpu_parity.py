@@ -354,6 +354,30 @@ def test_forward_tiny(tiny_params, T):
     assert_close(f64(delta)[same], ref["y"][same], f"forward tiny T={T}")
 
 
+def test_forward_timed_with_null_events(tiny_params):
+    """moe_forward_timed records only the events it is given (the timed bench region passes the two
+    around the up-projection): the result is moe_forward's bit for bit, and those two time a stage."""
+    _say("moe_forward_timed with two of six events")
+    from bench import HipEvents
+    dims, T = synth.TINY, 300
+    cd = cdims(dims)
+    x = synth.make_x(dims, T, DEV, seed=61)
+    layer = moe.MoELayer(cd, tiny_params)
+    ws = moe.workspace(cd, T)
+    d0, d1 = torch.empty_like(x), torch.empty_like(x)
+    moe.moe_forward(cd, layer.weights, T, x, d0, None, None, ws)
+    hev = HipEvents()
+    try:
+        evs = [None] * moe.MOE_FORWARD_EVENTS
+        evs[2], evs[3] = hev.create(2)
+        moe.moe_forward_timed(cd, layer.weights, T, x, d1, None, None, ws, evs)
+        torch.cuda.synchronize()
+        assert hev.ms(evs[2], evs[3]) > 0.0
+    finally:
+        hev.close()
+    assert torch.equal(d0, d1)
+
+
 def test_forward_is_deterministic(tiny_params):
     _say("moe_forward determinism")
     dims = synth.TINY
