@@ -41,7 +41,8 @@ Layout layout(const moe_dims& dm, int64_t T) {
   const size_t E = dm.n_experts, K = dm.topk, d = dm.d_model, I = dm.inter, t = (size_t)T;
   const size_t rows = t * K + t;
   const size_t nchunks = (t + PERM_CHUNK - 1) / PERM_CHUNK;
-  const int NT = ffn_tile_rows(T);
+  // the tile list is sized for the narrower of the e4m3 and bf16 tiles (more tiles)
+  const int NT = std::min(ffn_tile_rows(T), ffn_tile_rows(T, false, true));
   L.zpart = take((size_t)gate_ksplit(T, dm.d_model, dm.n_experts) * t * E * 4);
   L.idx = take(t * K * 4);
   L.w = take(t * K * 4);
@@ -337,8 +338,8 @@ int forward_impl(const moe_dims* dims, const float* gate_w, const float* gate_b,
                                  gate_ksplit(tokens, d.d_model, d.n_experts), idx, w, s)));
   record_event(ev, 1, s);
   // small batches: the permutation kernel also writes the FFN tile list
-  const PlanArgs plan{at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles), ffn_tile_rows(tokens), 1,
-                      ffn_plan_cap(tokens, d.topk, d.n_experts, true)};
+  const PlanArgs plan{at<int4>(workspace, L.tiles), at<int32_t>(workspace, L.n_tiles),
+                      ffn_tile_rows(tokens, false, bf16), 1, ffn_plan_cap(tokens, d.topk, d.n_experts, true, bf16)};
   bool planned = false;
   MOE_TRY(hip_status(launch_permute(idx, x, T, d.d_model, d.n_experts, d.topk, at<int32_t>(workspace, L.chunk_cnt),
                                     at<int32_t>(workspace, L.chunk_off), at<int32_t>(workspace, L.counts), offsets,

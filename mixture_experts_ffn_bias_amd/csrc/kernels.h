@@ -54,7 +54,8 @@ inline void record_event(hipEvent_t* ev, int i, hipStream_t s) {
 }
 
 // ffn.hip
-int ffn_tile_rows(int64_t T, bool dense = false);   // rows per FFN tile for this token count (dense: the MLP)
+// rows per FFN tile for this token count (dense: the MLP; bf16: bf16 expert weights)
+int ffn_tile_rows(int64_t T, bool dense = false, bool bf16 = false);
 int64_t ffn_max_tiles(int64_t T, int K, int E, int tile_rows);
 // E = K = 0 with `shared` set and row_token NULL runs one dense expert over
 // rows 0..T-1 (offsets is then not read).
@@ -88,7 +89,7 @@ hipError_t launch_ffn(const ExpertPtrs& routed, const ExpertPtrs* shared, int T,
 void ffn_dense_ksplit(int64_t T, int d, int I, int* up_ks, int* up_kper, int* dn_ks, int* dn_kper, int* up_stream,
                       int* up_planes);
 // routed tiles the plan may write (the tile list holds ffn_max_tiles entries)
-int ffn_plan_cap(int64_t T, int K, int E, bool has_shared);
+int ffn_plan_cap(int64_t T, int K, int E, bool has_shared, bool bf16 = false);
 
 // combine.hip
 hipError_t launch_combine(const int32_t* idx, const float* w, const int32_t* pair_row, const uint16_t* rows,

@@ -124,9 +124,11 @@ def assert_rows_close(gpu: np.ndarray, ref: np.ndarray, what: str, within_ulp: f
 
 def tile_rows(T: int, bf16: bool = False) -> int:
     """Rows per FFN tile of the routed layer for a batch of T tokens (the
-    library's choice): 32 up to 128 tokens, then 128 (e4m3 and bf16 expert
-    weights alike)."""
-    return 32 if T <= 128 else 128
+    library's choice): with e4m3 expert weights 32 up to 768 tokens, 64 up to
+    1280, then 128; with bf16 weights 32 up to 128 tokens, then 128."""
+    if bf16:
+        return 32 if T <= 128 else 128
+    return 32 if T <= 768 else (64 if T <= 1280 else 128)
 
 
 def tile_starts(count: int, T: int, bf16: bool = False):

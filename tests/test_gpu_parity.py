@@ -200,13 +200,17 @@ def _idx_with_counts(counts, T, K):
 
 
 @pytest.mark.parametrize("T,counts", [
-    # 32-row tiles (T <= 128): ragged tails and experts cut into two or three equal tiles
+    # 32-row tiles (T <= 768): ragged tails and experts cut into two or three equal tiles
     (100, [0, 1, 15, 16, 17, 31, 32, 33, 48, 49, 63, 65, 30, 0, 0, 0]),
-    # 128-row tiles: one to eight 16-row sub-tiles per wave row with ragged tails; 129 / 144 /
-    # 160 / 193 rows are cut into two equal 16-row-aligned tiles
+    # ... and into up to 15 tiles each
     (300, [0, 1, 15, 16, 17, 47, 49, 63, 65, 127, 128, 129, 144, 160, 193, 46]),
-    # ... 257 / 300 / 385 rows into three or four tiles
     (600, [0, 1, 33, 95, 96, 97, 192, 193, 257, 300, 385, 451, 300, 0, 0, 0]),
+    # 64-row tiles (769..1280 tokens): one to four sub-tiles with ragged tails, 65 / 129 rows cut
+    # into two or three tiles, 400..997 rows into 7 to 16
+    (1000, [0, 1, 15, 16, 17, 33, 63, 64, 65, 129, 400, 600, 700, 900, 997, 0]),
+    # 128-row tiles (more tokens): one to eight sub-tiles over the two wave rows with ragged
+    # tails, 129 / 193 rows in two equal 16-row-aligned tiles, 385..1300 rows in 4 to 11
+    (1300, [0, 1, 15, 16, 17, 63, 65, 127, 128, 129, 193, 385, 1000, 1300, 1300, 461]),
 ])
 def test_grouped_ffn_tile_edges(tiny_params, T, counts):
     _say(f"moe_grouped_ffn tile edges T={T}")

@@ -7,8 +7,8 @@ compares the outputs of a token sample with the oracle, evaluated in one call
 per layer so that each expert is dequantised once:
 
 * decode (64 tokens): every token;
-* prefill (4,096 tokens), skewed (16,384) and the prefill instance at 65,536
-  tokens: the first and the last permuted row of every touched expert, both
+* prefill (4,096 tokens), skewed (16,384) and the prefill instance at 500,
+  1,000 and 65,536 tokens: the first and the last permuted row of every touched expert, both
   sides of every boundary between the FFN tiles of an expert that is cut into
   several tiles (and of the shared expert's tiles), and seeded random tokens up
   to at least 256;
@@ -102,6 +102,20 @@ def test_prefill_workload_sampled_tokens(prefill_block):
     delta, gi, gw = _forward(w.dims, prefill_block, x)
     tok = sample_tokens(gi, w.dims.n_experts, w.tokens, 256, seed=1)
     _check_layer("prefill T=4096", w.dims, prefill_block, x, delta, gi, gw, tok)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [500, 1000])
+def test_prefill_weights_at_mid_batch_sizes(prefill_block, T):
+    """The prefill instance's weights at batch sizes between decode and
+    prefill: 32-row tiles at 500 tokens (experts of ~16 rows, some cut in
+    two), 64-row tiles at 1000."""
+    _say(f"prefill weights at T={T}")
+    w = synth.WORKLOADS["prefill"]
+    x = synth.make_x(w.dims, T, DEV, w.seed + T)
+    delta, gi, gw = _forward(w.dims, prefill_block, x)
+    tok = sample_tokens(gi, w.dims.n_experts, T, 256, seed=4)
+    _check_layer(f"prefill weights T={T}", w.dims, prefill_block, x, delta, gi, gw, tok)
 
 
 @pytest.mark.timeout(1200)
